@@ -17,8 +17,8 @@
  *     (bjdmk.com.cn):
  *       * data-loading section: a token is 576 dims; the first 512 are stored as
  *         e4m3 with 1x128 tile scales, the last 64 are RoPE dims kept in bf16; the
- *         kernel dequantises, concatenates, and multiplies in bf16 with fp32
- *         accumulation;
+ *         kernel dequantises to bf16, concatenates, and multiplies in bf16 with
+ *         fp32 accumulation (so the FP8 latent the attention sees is bf16);
  *       * scheduling section: long sequences are cut into splits computed
  *         separately;
  *       * combine section: each split leaves a partial o and lse, merged with lse.
@@ -109,11 +109,34 @@ int64_t oracle_token_bytes(int is_fp8) {
                 : (int64_t)ORACLE_D_QK * 2;
 }
 
+/* ---- FP8 element -> the bf16 value the matrix multiply uses ---------------- */
+
+/*
+ * Dequantisation of one FP8 element.  The source walk-through (data-loading
+ * section) has the kernel turn the 512 FP8 values back into bfloat16 and run
+ * the matrix multiplies in bf16, so the latent the attention sees is a bf16
+ * value.  Reading of the rounding: widen e4m3 to binary32 (exact), multiply by
+ * the binary32 scale with round-to-nearest-even, then round the binary32
+ * product to bf16 with round-to-nearest-even.  NaN stays NaN (quiet).
+ */
+uint16_t oracle_fp8_dequant_bf16(uint8_t code, float scale) {
+  float v = (float)oracle_e4m3fn_to_f64(code);
+  volatile float p = v * scale; /* binary32 multiply, round to nearest even */
+  float pf = p;
+  uint32_t u;
+  memcpy(&u, &pf, sizeof u);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0) return (uint16_t)((u >> 16) | 0x0040u);
+  {
+    uint32_t lsb = (u >> 16) & 1u;
+    uint32_t rounded = u + 0x7FFFu + lsb;
+    return (uint16_t)(rounded >> 16);
+  }
+}
+
 /*
  * The 576-dim latent of one stored token, widened to float64.
- * FP8: K[d] = e4m3(byte d) * scale[d / 128] for d < 512 (the product of a
- * 4-significant-bit value and a 24-bit scale is exact in float64), and the
- * RoPE dims are the stored bf16 values.
+ * FP8: K[d] = bf16(fp32(e4m3(byte d) * scale[d / 128])) for d < 512 (the
+ * dequantised value above), and the RoPE dims are the stored bf16 values.
  */
 void oracle_token_latent(const uint8_t* token, int is_fp8, double* k) {
   int d;
@@ -125,8 +148,8 @@ void oracle_token_latent(const uint8_t* token, int is_fp8, double* k) {
     return;
   }
   for (d = 0; d < ORACLE_FP8_DIMS; ++d) {
-    double scale = le_f32_to_f64(token + ORACLE_FP8_DIMS + 4 * (d / ORACLE_FP8_TILE));
-    k[d] = oracle_e4m3fn_to_f64(token[d]) * scale;
+    float scale = (float)le_f32_to_f64(token + ORACLE_FP8_DIMS + 4 * (d / ORACLE_FP8_TILE));
+    k[d] = oracle_bf16_to_f64(oracle_fp8_dequant_bf16(token[d], scale));
   }
   for (d = ORACLE_FP8_DIMS; d < ORACLE_D_QK; ++d) {
     const uint8_t* r = token + ORACLE_FP8_DIMS + 16 + 2 * (d - ORACLE_FP8_DIMS);
@@ -251,28 +274,6 @@ void oracle_mla_decode(const uint16_t* q, int B, int s_q, int h_q, const uint8_t
     oracle_attend(q + row * ORACLE_D_QK, kvcache, is_fp8, block_table + (int64_t)bb * max_blocks, pos, n, scale,
                   o + r * ORACLE_D_V, lse + r);
     free(pos);
-  }
-}
-
-/* ---- the bf16 value the GPU's FP8 decode must produce --------------------- */
-
-/*
- * Dequantisation contract for one FP8 element (the kernel dequantises to bf16
- * before the bf16 matrix multiply): widen e4m3 to binary32 (exact), multiply by
- * the binary32 scale with round-to-nearest-even, then round the binary32
- * product to bf16 with round-to-nearest-even.  NaN stays NaN (quiet).
- */
-uint16_t oracle_fp8_dequant_bf16(uint8_t code, float scale) {
-  float v = (float)oracle_e4m3fn_to_f64(code);
-  volatile float p = v * scale; /* binary32 multiply, round to nearest even */
-  float pf = p;
-  uint32_t u;
-  memcpy(&u, &pf, sizeof u);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0) return (uint16_t)((u >> 16) | 0x0040u);
-  {
-    uint32_t lsb = (u >> 16) & 1u;
-    uint32_t rounded = u + 0x7FFFu + lsb;
-    return (uint16_t)(rounded >> 16);
   }
 }
 

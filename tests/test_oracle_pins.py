@@ -22,12 +22,18 @@ import oracle
 
 
 def library_latents(prob):
-    """All stored tokens widened to float64 with torch's own conversions: [pool_tokens, 576]."""
+    """All stored tokens widened to float64 with torch's own conversions: [pool_tokens, 576].
+
+    FP8 dims 0..511 follow the dequantisation the source walk-through describes
+    (values turned back into bf16 before the bf16 multiply): torch's fp32
+    multiply by the scale, then torch's bf16 cast.
+    """
     if prob.is_fp8:
         kv = prob.kvcache.reshape(-1, mi.FP8_TOKEN_BYTES)
-        vals = kv[:, :512].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
-        scales = kv[:, 512:528].contiguous().view(torch.float32).to(torch.float64)
-        vals = vals * scales.repeat_interleave(128, dim=1)
+        vals = kv[:, :512].contiguous().view(torch.float8_e4m3fn).to(torch.float32)
+        scales = kv[:, 512:528].contiguous().view(torch.float32)
+        # dequantised to bf16 before the bf16 multiply: fp32 product, then bf16
+        vals = (vals * scales.repeat_interleave(128, dim=1)).to(torch.bfloat16).to(torch.float64)
         rope = kv[:, 528:].contiguous().view(torch.bfloat16).to(torch.float64)
         return torch.cat([vals, rope], dim=1)
     return prob.kvcache.reshape(-1, mi.D_QK).to(torch.float64)
@@ -111,6 +117,7 @@ def test_fp8_token_layout_handbuilt(golden):
     k = oracle.token_latent(tok, True)
     e4 = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     tile = lay["scale_tile_dims"]
+    # every code times these scales is exact in bf16, so the decode is exact
     expect = np.concatenate([e4 * np.repeat(scales.astype(np.float64), tile), rope.astype(np.float64)])
     assert np.array_equal(k, expect)
 
@@ -137,11 +144,12 @@ def test_fp8_writer_roundtrip():
             if s == 0.0:
                 assert np.all(kr == 0.0)
                 continue
+            # e4m3 rounding (2^-4 relative on normals, scale 2^-10 on subnormals), then bf16 (2^-9)
             normal = np.abs(xr) >= s * 2.0 ** -6
-            assert np.all(np.abs(kr - xr)[normal] <= 2.0 ** -4 * np.abs(xr)[normal] + 1e-300)
-            assert np.all(np.abs(kr - xr)[~normal] <= s * 2.0 ** -10 * (1 + 1e-6))
+            assert np.all(np.abs(kr - xr)[normal] <= (2.0 ** -4 + 2.0 ** -8) * np.abs(xr)[normal] + 1e-300)
+            assert np.all(np.abs(kr - xr)[~normal] <= s * 2.0 ** -10 * (1 + 1e-6) + 2.0 ** -9 * np.abs(kr)[~normal])
             j = int(np.argmax(np.abs(xr)))
-            assert abs(abs(kr[j]) - abs(xr[j])) <= np.spacing(np.float32(abs(xr[j])))
+            assert abs(abs(kr[j]) - abs(xr[j])) <= 2.0 ** -8 * abs(xr[j])
 
 
 def test_fp8_dequant_contract_matches_torch():
