@@ -1,0 +1,12 @@
+"""MI355X (gfx950) MLA decoding over a paged latent KV cache.
+
+The decode path is the HIP library libmla_decode.so (C ABI in
+include/mla_decode.h): a scheduler kernel, a split-KV decode kernel and an lse
+combine kernel.  This package holds its sources (csrc/), its build script and a
+thin ctypes binding with the same function names.
+"""
+from .binding import (Metadata, MlaError, mla_debug_dequant_fp8, mla_decode_with_kvcache, mla_get_metadata,
+                      mla_get_metadata_size, mla_last_error, lib, LIB_PATH)
+
+__all__ = ["Metadata", "MlaError", "mla_debug_dequant_fp8", "mla_decode_with_kvcache", "mla_get_metadata",
+           "mla_get_metadata_size", "mla_last_error", "lib", "LIB_PATH"]

@@ -1,0 +1,215 @@
+// Host side of the C ABI (include/mla_decode.h): argument validation, sizing,
+// workspace carving and kernel launches.  Validation happens before any HIP
+// call, so a rejected call launches nothing and touches no device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+
+#include "../../include/mla_decode.h"
+#include "mla_common.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Smallest number of tiles a worker takes: a split costs a Q reload and a
+// partial-output round trip, so very short splits are not worth it.
+int min_tiles_for(int is_fp8, int topk) {
+  (void)is_fp8;
+  (void)topk;
+  return 2;
+}
+
+struct Shape {
+  int n_streams, R, RT, n_rt;
+};
+
+int shape_of(int B, int s_q, int h_q, int h_kv, int topk, Shape* s) {
+  if (B < 1 || s_q < 1 || h_q < 1) return fail(MLA_ERR_INVALID_ARG, "B, s_q and h_q must be >= 1 (got %d, %d, %d)", B, s_q, h_q);
+  if (h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv must be 1 (got %d)", h_kv);
+  if (topk < 0) return fail(MLA_ERR_INVALID_ARG, "topk must be >= 0 (got %d)", topk);
+  const int64_t streams = topk > 0 ? (int64_t)B * s_q : (int64_t)B;
+  const int64_t R = topk > 0 ? (int64_t)h_q : (int64_t)s_q * h_q;
+  if (streams > (1 << 24) || R > (1 << 16)) return fail(MLA_ERR_UNSUPPORTED, "too many streams or rows per stream");
+  s->n_streams = (int)streams;
+  s->R = (int)R;
+  s->RT = mla::kRowTile;
+  s->n_rt = (s->R + s->RT - 1) / s->RT;
+  return MLA_OK;
+}
+
+std::mutex g_cu_mu;
+int g_cu_count[64] = {0};
+
+int device_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_cu_mu);
+  if (dev >= 0 && dev < 64 && g_cu_count[dev] > 0) {
+    *out = g_cu_count[dev];
+    return MLA_OK;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  if (dev >= 0 && dev < 64) g_cu_count[dev] = n;
+  *out = n;
+  return MLA_OK;
+}
+
+int resolve_workers(int num_workers, const Shape& s, int* W) {
+  if (num_workers < 0) return fail(MLA_ERR_INVALID_ARG, "num_workers must be >= 0");
+  if (num_workers > 0) {
+    *W = num_workers;
+    return MLA_OK;
+  }
+  int cus = 0;
+  const int rc = device_cus(&cus);
+  if (rc != MLA_OK) return rc;
+  int w = cus / s.n_rt;
+  if (w >= 8) w &= ~7;  // keep a worker's row tiles on one XCD
+  *W = w < 1 ? 1 : w;
+  return MLA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+void sizes(const Shape& s, int W, size_t* meta, size_t* part_o, size_t* ws) {
+  const size_t max_splits = (size_t)W + (size_t)s.n_streams;
+  *meta = (size_t)mla::meta_words(W, s.n_streams) * sizeof(int32_t);
+  *part_o = align_up(max_splits * (size_t)s.R * mla::kDV * sizeof(float));
+  *ws = *part_o + align_up(max_splits * (size_t)s.R * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+MLA_API const char* mla_last_error(void) { return g_err; }
+
+MLA_API int mla_get_metadata_size(int B, int s_q, int h_q, int h_kv, int topk, int num_workers, size_t* metadata_bytes,
+                                  size_t* workspace_bytes, int* num_workers_out) {
+  g_err[0] = 0;
+  if (!metadata_bytes || !workspace_bytes) return fail(MLA_ERR_INVALID_ARG, "null size output pointer");
+  Shape s;
+  int rc = shape_of(B, s_q, h_q, h_kv, topk, &s);
+  if (rc != MLA_OK) return rc;
+  int W = 0;
+  rc = resolve_workers(num_workers, s, &W);
+  if (rc != MLA_OK) return rc;
+  size_t meta, part_o, ws;
+  sizes(s, W, &meta, &part_o, &ws);
+  *metadata_bytes = meta;
+  *workspace_bytes = ws;
+  if (num_workers_out) *num_workers_out = W;
+  return MLA_OK;
+}
+
+MLA_API int mla_get_metadata(const int32_t* cache_seqlens, int B, int s_q, int h_q, int h_kv, int topk, int is_fp8,
+                             int num_workers, int32_t* metadata, size_t metadata_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!cache_seqlens || !metadata) return fail(MLA_ERR_INVALID_ARG, "null cache_seqlens or metadata");
+  if (is_fp8 != 0 && is_fp8 != 1) return fail(MLA_ERR_INVALID_ARG, "is_fp8 must be 0 or 1");
+  Shape s;
+  int rc = shape_of(B, s_q, h_q, h_kv, topk, &s);
+  if (rc != MLA_OK) return rc;
+  int W = 0;
+  rc = resolve_workers(num_workers, s, &W);
+  if (rc != MLA_OK) return rc;
+  size_t meta, part_o, ws;
+  sizes(s, W, &meta, &part_o, &ws);
+  if (metadata_bytes < meta)
+    return fail(MLA_ERR_BUFFER_TOO_SMALL, "metadata needs %zu bytes, got %zu", meta, metadata_bytes);
+  const hipError_t e = mla::launch_sched(cache_seqlens, B, s_q, h_q, topk, W, min_tiles_for(is_fp8, topk), metadata,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "scheduler launch");
+  return MLA_OK;
+}
+
+MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_blocks, const int32_t* block_table,
+                                    int max_blocks, const int32_t* cache_seqlens, int B, int s_q, int h_q, int h_kv,
+                                    int d_qk, int d_v, float softmax_scale, const int32_t* metadata,
+                                    size_t metadata_bytes, int num_workers, const int32_t* indices, int topk,
+                                    int is_fp8, void* workspace, size_t workspace_bytes, void* o, float* lse,
+                                    void* stream) {
+  g_err[0] = 0;
+  if (!q || !kvcache || !block_table || !cache_seqlens || !metadata || !o || !lse || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (d_qk != mla::kDQK || d_v != mla::kDV)
+    return fail(MLA_ERR_UNSUPPORTED, "only d_qk = 576 and d_v = 512 are supported (got %d, %d)", d_qk, d_v);
+  if (num_blocks < 1 || max_blocks < 1) return fail(MLA_ERR_INVALID_ARG, "num_blocks and max_blocks must be >= 1");
+  if (is_fp8 != 0 && is_fp8 != 1) return fail(MLA_ERR_INVALID_ARG, "is_fp8 must be 0 or 1");
+  if (topk > 0 && !indices) return fail(MLA_ERR_INVALID_ARG, "topk > 0 needs indices");
+  if (topk == 0 && indices) return fail(MLA_ERR_INVALID_ARG, "indices given with topk = 0");
+  if ((((uintptr_t)q) | ((uintptr_t)kvcache) | ((uintptr_t)o) | ((uintptr_t)workspace)) & 15)
+    return fail(MLA_ERR_INVALID_ARG, "q, kvcache, o and workspace must be 16-byte aligned");
+  Shape s;
+  int rc = shape_of(B, s_q, h_q, h_kv, topk, &s);
+  if (rc != MLA_OK) return rc;
+  int W = 0;
+  rc = resolve_workers(num_workers, s, &W);
+  if (rc != MLA_OK) return rc;
+  size_t meta, part_o, ws;
+  sizes(s, W, &meta, &part_o, &ws);
+  if (metadata_bytes < meta)
+    return fail(MLA_ERR_BUFFER_TOO_SMALL, "metadata needs %zu bytes, got %zu", meta, metadata_bytes);
+  if (workspace_bytes < ws)
+    return fail(MLA_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", ws, workspace_bytes);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)mla::kDQK);
+
+  mla::DecodeParams p;
+  p.q = (const uint16_t*)q;
+  p.kv = (const uint8_t*)kvcache;
+  p.block_table = block_table;
+  p.seqlens = cache_seqlens;
+  p.indices = indices;
+  p.meta = metadata;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace + part_o);
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.max_blocks = max_blocks;
+  p.topk = topk;
+  p.B = B;
+  p.s_q = s_q;
+  p.h_q = h_q;
+  p.R_stream = s.R;
+  p.n_streams = s.n_streams;
+  p.n_rt = s.n_rt;
+  p.W = W;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = mla::launch_decode(p, is_fp8 != 0, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  e = mla::launch_combine(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MLA_OK;
+}
+
+MLA_API int mla_debug_dequant_fp8(const uint8_t* tokens, int64_t n, void* out, void* stream) {
+  g_err[0] = 0;
+  if (!tokens || !out) return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (n < 0) return fail(MLA_ERR_INVALID_ARG, "n must be >= 0");
+  if ((((uintptr_t)tokens) | ((uintptr_t)out)) & 15) return fail(MLA_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  if (n == 0) return MLA_OK;
+  const hipError_t e = mla::launch_debug_dequant(tokens, n, (uint16_t*)out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "dequant launch");
+  return MLA_OK;
+}
+
+}  // extern "C"

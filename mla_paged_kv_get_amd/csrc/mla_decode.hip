@@ -1,0 +1,418 @@
+// Split-KV decode kernel for MLA over a paged latent cache (gfx950).
+//
+// What it computes: for each query row, softmax(scale * q K^T) V over the
+// attended tokens of its stream, where a token's 576-dim latent is K and its
+// first 512 dims are V (FlashMLA source walk-through, data-loading section), and
+// the natural log-sum-exp of the scaled scores.  Each worker processes the KV
+// tile range the scheduler gave it; a stream handled by one worker gets its
+// final o and lse here, otherwise each split leaves a normalised partial o and
+// its lse for the combine kernel (same page, scheduling and combine sections).
+//
+// Mapping to the hardware.  One workgroup (4 waves, one per SIMD) owns 64 query
+// rows of one stream; the chip runs one such workgroup per compute unit.  Waves
+// 2 r and 2 r + 1 ... are paired as (row block rb = wave & 1, half hf =
+// wave >> 1): both waves of a pair own the same 32 rows; the hf wave keeps half
+// of the Q dims in VGPRs (dims 256 hf .. + 256 and 512 + 32 hf .. + 32, 18 bf16x8
+// fragments) and half of the O^T columns (256 hf .. + 256) in AGPRs.
+// Per 32-token sub-tile of the KV stream:
+//   1. the page's bf16 rows are staged in a swizzled LDS tile (BF16: direct
+//      global->LDS 16-byte loads; FP8: 16-byte loads into VGPRs, e4m3 -> fp32
+//      (exact) * scale (RNE) -> bf16 (RNE), then LDS); three buffers keep two
+//      sub-tiles in flight behind the one being computed;
+//   2. each wave computes its partial S^T = K Q^T over its half of the dims on
+//      v_mfma_f32_32x32x16_bf16 (the K tile is the A operand), the pair swaps the
+//      partials through LDS and both add them in the same order, so both hold the
+//      same scores;
+//   3. online softmax in the log2 domain, lane-local (S^T puts query row
+//      lane % 32 in every lane's accumulator column) with a lazy reference
+//      maximum: the accumulators are rescaled only when a row maximum grows by
+//      more than 2^8, which keeps P <= 256 and makes rescales rare;
+//   4. O^T += V^T P^T on the same MFMA: P goes from the score registers straight
+//      into the B operand, V^T comes from the token-major tile through
+//      ds_read_b64_tr_b16.
+// Tokens that no row attends (page tails, -1 indices) are loaded from a static
+// zero token, so every wave issues the same number of loads per sub-tile and
+// their scores are masked to -inf.
+#include "mla_device.hpp"
+
+namespace mla {
+
+// A token of zeros: the source for slots no query row attends.
+__device__ __attribute__((aligned(64))) uint8_t g_zero_token[kBf16TokenBytes] = {0};
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescaleLog2 = 8.0f;
+constexpr int kSub = 32;                               // tokens per sub-tile
+constexpr int kSubBytes = kSub * kBf16TokenBytes;      // 36864
+constexpr int kNBuf = 3;
+constexpr int kXOffset = kNBuf * kSubBytes;            // S exchange: [2][4 waves][64 lanes][16 f32]
+constexpr int kXBytes = 4 * 64 * 16 * 4;
+constexpr int kTokOffset = kXOffset + 2 * kXBytes;     // int32 tokidx[4][32]
+constexpr int kMaskOffset = kTokOffset + 4 * kSub * 4;  // uint32 vmask[4]
+constexpr int kLdsBytes = kMaskOffset + 4 * 4;
+constexpr int kBf16LoadsPerThread = kSubBytes / 16 / kThreads;  // 9
+
+// FP8 registers of one sub-tile for this thread: token tid / 8, code chunks
+// j + 8 i (i = 0..3, j = tid % 8; chunk i uses scale i), the four scales and
+// RoPE chunk j.
+struct RawFp8 {
+  u32x4 v[4];
+  u32x4 sc;
+  u32x4 r;
+};
+
+template <bool FP8, bool SPARSE>
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+  MLA_LDS float* xbuf = (MLA_LDS float*)(smem + kXOffset);
+  MLA_LDS int32_t* tokidx = (MLA_LDS int32_t*)(smem + kTokOffset);
+  MLA_LDS uint32_t* vmask = (MLA_LDS uint32_t*)(smem + kMaskOffset);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;    // lane half (k-group of the MFMA operands)
+  const int l32 = lane & 31;  // query row within the row block
+  const int rb = wave & 1;    // row block
+  const int hf = wave >> 1;   // half of the dims / columns
+  const int partner = wave ^ 2;
+
+  // workgroup -> (worker, row tile); the row tiles of one worker share an XCD
+  int w, rt;
+  {
+    const int g = blockIdx.x;
+    if (p.n_rt == 1) {
+      w = g;
+      rt = 0;
+    } else if ((p.W & 7) == 0) {
+      const int grp = g / (8 * p.n_rt), rem = g % (8 * p.n_rt);
+      rt = rem >> 3;
+      w = grp * 8 + (rem & 7);
+    } else {
+      w = g / p.n_rt;
+      rt = g % p.n_rt;
+    }
+  }
+  const int32_t* ent = p.meta + kMetaHeader + (int64_t)w * kSchedStride;
+  const int bs = ent[0], bt0 = ent[1], es = ent[2], et = ent[3], split0 = ent[4];
+  const int32_t* split_off = p.meta + meta_split_offset(p.W);
+  const int32_t* first = p.meta + meta_tile_first(p.W, p.n_streams);
+  const int tok_bytes = FP8 ? kFp8TokenBytes : kBf16TokenBytes;
+
+  // ---- per-lane LDS offsets (independent of the sub-tile) ---------------------
+  // K operand: token l32, chunk c(kk) = 32 hf + 2 kk + h for kk < 16, and
+  // 64 + 4 hf + 2 (kk - 16) + h for kk = 16, 17.
+  const int ksw = tile_swizzle(l32);
+  int kofs[4], kofs_r[2];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) kofs[m] = l32 * kBf16TokenBytes + 32 * hf * 16 + (((2 * m + h) ^ ksw) << 4);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) kofs_r[m] = l32 * kBf16TokenBytes + ((64 + ((4 * hf + 2 * m + h) ^ ksw)) << 4);
+  // V^T operand (transposed reads): [s2][e4][parity of the column block]
+  int vofs[2][2][2];
+  {
+    const int tl = 4 * h + ((lane & 15) >> 2);
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int e4 = 0; e4 < 2; ++e4) {
+        const int tok = 16 * s2 + 8 * e4 + tl;
+        const int sw = tile_swizzle(tok);
+        const int sb = sw >> 2;
+        const int base = tok * kBf16TokenBytes + 8 * hf * 64 + ((cl ^ (sw & 3)) << 4) + 8 * (lane & 1);
+        vofs[s2][e4][0] = base + 64 * sb;
+        vofs[s2][e4][1] = base - 64 * sb;
+      }
+  }
+
+  for (int stream = bs; stream <= es && stream < p.n_streams; ++stream) {
+    const int ntiles = first[stream + 1] - first[stream];
+    const int lo = stream == bs ? bt0 : 0;
+    const int hi = stream == es ? et : ntiles;
+    if (hi <= lo) continue;
+    const int sid = stream == bs ? split0 : split_off[stream];
+    const bool final_out = (split_off[stream + 1] - split_off[stream]) == 1;
+
+    const int b = SPARSE ? stream / p.s_q : stream;
+    const int64_t row_base = (int64_t)stream * p.R_stream;
+    const int seqlen = p.seqlens[b];
+    const int32_t* bt_row = p.block_table + (int64_t)b * p.max_blocks;
+    const int32_t* idx_row = SPARSE ? p.indices + (int64_t)stream * p.topk : nullptr;
+    // sub-tiles [u0, u1): 32 tokens (dense) or 32 index slots (sparse) each
+    const int limit = SPARSE ? p.topk : seqlen;
+    const int u0 = 2 * lo;
+    const int u1 = min(2 * hi, (limit + kSub - 1) / kSub);
+
+    const int row = rt * 64 + rb * kWaveRows + l32;
+    const bool row_ok = row < p.R_stream;
+
+    // Q fragments: dims 256 hf + 16 kk + 8 h (kk < 16), 512 + 32 hf + 16 (kk - 16) + 8 h
+    bf16x8 qf[18];
+    {
+      const uint16_t* qrow = p.q + (row_base + (row_ok ? row : 0)) * kDQK + 8 * h;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) {
+        const int d = kk < 16 ? 256 * hf + 16 * kk : 512 + 32 * hf + 16 * (kk - 16);
+        u32x4 v = *(const u32x4*)(qrow + d);
+        if (!row_ok) v = u32x4{0, 0, 0, 0};
+        qf[kk] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+
+    f32x16 acc[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[cb][e] = 0.f;
+    float m_ref = kNegInf, l_sum = 0.f;
+
+    // ---- sparse index pipeline (wave 0, lanes 0..31) -----------------------------
+    auto idx_at = [&](int u) -> int {
+      const int slot = u * kSub + l32;
+      return (u < u1 && slot < p.topk) ? idx_row[slot] : -1;
+    };
+    auto tok_of = [&](int idx) -> int { return idx >= 0 ? bt_row[idx >> 6] * kPage + (idx & 63) : -1; };
+    auto publish = [&](int u, int tok) {
+      const uint64_t m = __ballot(tok >= 0);
+      if (lane < kSub) tokidx[(u & 3) * kSub + lane] = tok;
+      if (lane == 0) vmask[u & 3] = (uint32_t)m;
+    };
+    // ---- staging of sub-tile u into buffer `buf` -------------------------------
+    // page: the cache page of sub-tile u (dense; prefetched by the caller)
+    auto token_ptr = [&](int u, int t, int page) -> const uint8_t* {
+      if (SPARSE) {
+        const int tok = tokidx[(u & 3) * kSub + t];
+        return tok >= 0 ? p.kv + (int64_t)tok * tok_bytes : g_zero_token;
+      }
+      if (u * kSub + t >= seqlen) return g_zero_token;
+      return p.kv + ((int64_t)page * kPage + (u & 1) * kSub + t) * tok_bytes;
+    };
+    auto stage_bf16 = [&](int u, int page, MLA_LDS char* buf) {
+#pragma unroll
+      for (int k = 0; k < kBf16LoadsPerThread; ++k) {
+        const int inst = wave * kBf16LoadsPerThread + k;
+        const int s = inst * 64 + lane;
+        const int t = s / kTokenChunks;
+        const int c = (s - t * kTokenChunks) ^ tile_swizzle(t);
+        __builtin_amdgcn_global_load_lds((const void*)(token_ptr(u, t, page) + c * 16),
+                                         (MLA_LDS void*)(buf + inst * 1024), 16, 0, 0);
+      }
+    };
+    auto load_fp8 = [&](int u, int page, RawFp8& r) {
+      const int t = tid >> 3, j = tid & 7;
+      const uint8_t* pt = token_ptr(u, t, page);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.v[i] = *(const u32x4*)(pt + 16 * (j + 8 * i));
+      r.sc = *(const u32x4*)(pt + kFp8Dims);
+      r.r = *(const u32x4*)(pt + kFp8Dims + 16 + 16 * j);
+    };
+    auto store_fp8 = [&](const RawFp8& r, MLA_LDS char* buf) {
+      const int t = tid >> 3, j = tid & 7;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = j + 8 * i;
+        u32x4 lo, hi;
+        dequant16(r.v[i], pick_scale(r.sc, i), lo, hi);
+        *(MLA_LDS u32x4*)(buf + tile_slot(t, 2 * c) * 16) = lo;
+        *(MLA_LDS u32x4*)(buf + tile_slot(t, 2 * c + 1) * 16) = hi;
+      }
+      *(MLA_LDS u32x4*)(buf + tile_slot(t, 64 + j) * 16) = r.r;
+    };
+    auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((u - u0) % kNBuf) * kSubBytes; };
+    auto page_of = [&](int u) -> int { return (!SPARSE && u < u1) ? bt_row[u >> 1] : 0; };
+
+    // ---- one sub-tile of compute ------------------------------------------------
+    auto compute = [&](int u, MLA_LDS char* buf) {
+      // partial S^T over this wave's dims
+      f32x16 s = {};
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) {
+        const int off = kk < 16 ? kofs[kk & 3] + (kk >> 2) * 128 : kofs_r[kk - 16];
+        const bf16x8 kf = *(MLA_LDS bf16x8*)(buf + off);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
+      }
+      // swap partial scores with the partner wave
+      MLA_LDS f32x4* xo = (MLA_LDS f32x4*)(xbuf + (((u & 1) * 4 + wave) * 64 + lane) * 16);
+      MLA_LDS f32x4* xp = (MLA_LDS f32x4*)(xbuf + (((u & 1) * 4 + partner) * 64 + lane) * 16);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) xo[q4] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+      __syncthreads();
+      float x[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 o = xp[q4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // both waves add (hf 0 partial) + (hf 1 partial)
+          const float mine = s[4 * q4 + e], theirs = o[e];
+          x[4 * q4 + e] = hf == 0 ? mine + theirs : theirs + mine;
+        }
+      }
+      // mask and scale: lane holds row l32, tokens 8 (e / 4) + 4 h + e % 4
+      const uint32_t tmask = SPARSE ? vmask[u & 3] : 0u;
+      const int vcount = SPARSE ? kSub : seqlen - u * kSub;
+      float mx = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tok = 8 * (e >> 2) + 4 * h + (e & 3);
+        const bool ok = SPARSE ? ((tmask >> tok) & 1u) != 0 : tok < vcount;
+        x[e] = ok ? x[e] * p.scale_log2 : kNegInf;
+        mx = fmaxf(mx, x[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_ref, mx);
+      const bool need = m_new > m_ref + kRescaleLog2;  // true on the first finite score too
+      if (__ballot(need) != 0) {
+        const float alpha = need ? (m_ref == kNegInf ? 0.f : exp2f(m_ref - m_new)) : 1.f;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[cb][e] *= alpha;
+        }
+        l_sum *= alpha;
+        m_ref = need ? m_new : m_ref;
+      }
+      const float msafe = m_ref == kNegInf ? 0.f : m_ref;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x[e] = exp2f(x[e] - msafe);
+        l_sum += x[e];
+      }
+      // O^T += V^T P^T over two 16-token k-steps
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)x[8 * s2 + e];
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][0][cb & 1] + 64 * cb));
+          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][1][cb & 1] + 64 * cb));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[cb], 0, 0, 0);
+        }
+      }
+    };
+
+    // ---- prologue: index data for u0 .. u0 + 2, stage u0 and u0 + 1 -------------
+    int idx_pref = -1;  // sparse: index of slot l32 of sub-tile u + 3 (wave 0)
+    if (SPARSE) {
+      if (wave == 0) {
+        publish(u0, tok_of(idx_at(u0)));
+        publish(u0 + 1, tok_of(idx_at(u0 + 1)));
+        publish(u0 + 2, tok_of(idx_at(u0 + 2)));
+        idx_pref = idx_at(u0 + 3);
+      }
+      __syncthreads();
+    }
+    RawFp8 rawA, rawB;  // FP8: the next two sub-tiles in flight in VGPRs
+    if (FP8) {
+      load_fp8(u0, page_of(u0), rawA);
+      store_fp8(rawA, buffer(u0));
+      if (u0 + 1 < u1) load_fp8(u0 + 1, page_of(u0 + 1), rawA);
+    } else {
+      stage_bf16(u0, page_of(u0), buffer(u0));
+      if (u0 + 1 < u1) {
+        stage_bf16(u0 + 1, page_of(u0 + 1), buffer(u0 + 1));
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // sub-tile u0 has landed
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    }
+    int page_pref = page_of(u0 + 2);  // dense: page of sub-tile u + 2
+    __syncthreads();
+
+    // ---- main loop: compute u while u + 1 and u + 2 stream in ---------------------
+    // next: registers holding sub-tile u + 1 (FP8); fill: receives sub-tile u + 2
+    auto step = [&](int u, RawFp8& next, RawFp8& fill) {
+      int tok_pref = -1;
+      if (SPARSE && wave == 0) {
+        tok_pref = tok_of(idx_pref);  // sub-tile u + 3; its index came last round
+        idx_pref = idx_at(u + 4);
+      }
+      const int page2 = page_pref;
+      page_pref = page_of(u + 3);
+      __builtin_amdgcn_sched_barrier(0);  // index loads stay ahead of the tile loads
+      if (u + 2 < u1) {
+        if (FP8)
+          load_fp8(u + 2, page2, fill);
+        else
+          stage_bf16(u + 2, page2, buffer(u + 2));
+      }
+      compute(u, buffer(u));
+      if (FP8 && u + 1 < u1) store_fp8(next, buffer(u + 1));
+      if (SPARSE && wave == 0) publish(u + 3, tok_pref);
+      if (!FP8) {
+        if (u + 2 < u1)
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // u + 1 landed, u + 2 may fly
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
+    };
+    for (int u = u0; u < u1; u += 2) {
+      step(u, rawA, rawB);
+      if (u + 1 < u1) step(u + 1, rawB, rawA);
+    }
+
+    // ---- epilogue -------------------------------------------------------------------
+    l_sum += __shfl_xor(l_sum, 32);
+    const bool empty = !(l_sum > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_sum;
+    const float lse_v = empty ? kNegInf : (m_ref + __log2f(l_sum)) * 0.69314718055994531f;
+    if (row_ok) {
+      if (final_out) {
+        uint16_t* orow = p.o + (row_base + row) * kDV + 256 * hf + 4 * h;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bf16x2 v0, v1;
+            v0.x = (__bf16)(acc[cb][4 * i + 0] * inv);
+            v0.y = (__bf16)(acc[cb][4 * i + 1] * inv);
+            v1.x = (__bf16)(acc[cb][4 * i + 2] * inv);
+            v1.y = (__bf16)(acc[cb][4 * i + 3] * inv);
+            *(u32x2*)(orow + cb * 32 + 8 * i) = u32x2{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1)};
+          }
+        if (h == 0 && hf == 0) p.lse[row_base + row] = lse_v;
+      } else {
+        float* prow = p.part_o + ((int64_t)sid * p.R_stream + row) * kDV + 256 * hf + 4 * h;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *(f32x4*)(prow + cb * 32 + 8 * i) = f32x4{acc[cb][4 * i] * inv, acc[cb][4 * i + 1] * inv,
+                                                     acc[cb][4 * i + 2] * inv, acc[cb][4 * i + 3] * inv};
+        if (h == 0 && hf == 0) p.part_lse[(int64_t)sid * p.R_stream + row] = lse_v;
+      }
+    }
+    __syncthreads();  // LDS is reused by the next piece
+  }
+}
+
+template <bool FP8, bool SPARSE>
+hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
+  static bool attr_set = false;
+  auto kern = mla_decode_kernel<FP8, SPARSE>;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(p.W * p.n_rt), dim3(kThreads), kLdsBytes, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, bool is_fp8, hipStream_t stream) {
+  const bool sparse = p.topk > 0;
+  if (is_fp8) return sparse ? launch_variant<true, true>(p, stream) : launch_variant<true, false>(p, stream);
+  return sparse ? launch_variant<false, true>(p, stream) : launch_variant<false, false>(p, stream);
+}
+
+}  // namespace mla

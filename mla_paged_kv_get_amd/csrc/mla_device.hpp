@@ -1,0 +1,60 @@
+// Device helpers shared by the decode and debug kernels: the LDS layout of a
+// 64-token tile and the FP8 -> bf16 decode of the 656-byte token.
+#pragma once
+
+#include "mla_common.hpp"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define MLA_LDS __attribute__((address_space(3)))
+
+// LDS tile layout: token t of the page occupies 72 consecutive 16-byte slots
+// (t * 72 ...); 16-byte chunk c of its bf16 row is stored at slot
+// t * 72 + (c ^ swizzle(t)).  The XOR only touches the low three chunk bits, so
+// chunks 0..63 and 64..71 stay in place as groups.  swizzle(t) takes
+// u = (t / 2) % 8 to ((u & 1) << 2) | (u >> 1), which keeps both access
+// patterns of the decode kernel free of bank conflicts on a 64-bank LDS:
+//  - 16 consecutive tokens reading the same chunk (the K operand), and
+//  - 4 consecutive tokens (aligned to 4) reading 4 aligned chunks (the
+//    transposed V operand).
+__device__ __forceinline__ int tile_swizzle(int t) {
+  const int u = (t >> 1) & 7;
+  return ((u & 1) << 2) | (u >> 1);
+}
+__device__ __forceinline__ int tile_slot(int t, int chunk) { return t * kTokenChunks + (chunk ^ tile_swizzle(t)); }
+
+// Four e4m3fn codes (little-endian bytes of w) times `scale`, each rounded to
+// fp32 (RNE) and then to bf16 (RNE); returns the four bf16 packed in two words.
+__device__ __forceinline__ u32x2 dequant4(uint32_t w, float scale) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);  // bytes 0, 1 (exact)
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);   // bytes 2, 3
+  bf16x2 lo, hi;
+  lo.x = (__bf16)(a.x * scale);
+  lo.y = (__bf16)(a.y * scale);
+  hi.x = (__bf16)(b.x * scale);
+  hi.y = (__bf16)(b.y * scale);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+// 16 codes (one 16-byte chunk of the FP8 token) -> 16 bf16 in two uint4.
+__device__ __forceinline__ void dequant16(u32x4 codes, float scale, u32x4& lo, u32x4& hi) {
+  const u32x2 a = dequant4(codes.x, scale), b = dequant4(codes.y, scale);
+  const u32x2 c = dequant4(codes.z, scale), d = dequant4(codes.w, scale);
+  lo = u32x4{a.x, a.y, b.x, b.y};
+  hi = u32x4{c.x, c.y, d.x, d.y};
+}
+
+__device__ __forceinline__ float pick_scale(const u32x4& s, int i) {
+  const uint32_t v = i == 0 ? s.x : i == 1 ? s.y : i == 2 ? s.z : s.w;
+  return __builtin_bit_cast(float, v);
+}
+
+}  // namespace mla

@@ -1,0 +1,161 @@
+// Scheduler kernel: spreads the decode step's (stream, KV tile range) work
+// evenly over W workers ahead of time, so the decode kernel only follows a
+// precomputed plan (FlashMLA source walk-through, scheduling section: a small
+// kernel divides (request, KV block range) units among all compute units before
+// the main kernel runs; long sequences become several splits).
+//
+// Rule (deterministic, integer only):
+//   streams: dense -> one per request with ceil(seqlen_b / 64) tiles;
+//            sparse -> one per (request, query token) with ceil(topk / 64) tiles;
+//   N = total tiles, q = max(ceil(N / W), min_tiles, 1);
+//   worker w owns global tiles [w q, min((w + 1) q, N)) of the streams laid end
+//   to end; each stream's splits are the workers that meet it, in worker order.
+// One workgroup of 256 threads: chunked prefix sums over the streams, then one
+// binary search per worker.
+#include "mla_common.hpp"
+
+namespace mla {
+
+namespace {
+
+constexpr int kSchedThreads = 256;
+
+__device__ __forceinline__ int64_t stream_tiles(const int32_t* seqlens, int topk, int i) {
+  const int64_t len = topk > 0 ? (int64_t)topk : (int64_t)seqlens[i];
+  return len > 0 ? (len + kPage - 1) / kPage : 0;
+}
+
+// Exclusive scan of part[0..256) in place by one thread; returns the total.
+__device__ int64_t scan_parts(int64_t* part) {
+  int64_t acc = 0;
+  for (int k = 0; k < kSchedThreads; ++k) {
+    const int64_t t = part[k];
+    part[k] = acc;
+    acc += t;
+  }
+  return acc;
+}
+
+// First index in [0, n) with a[idx] > x (n if none); a non-decreasing.
+__device__ int upper_bound(const int32_t* a, int n, int64_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)a[mid] > x)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t* __restrict__ seqlens, int B, int s_q,
+                                                                  int h_q, int topk, int W, int min_tiles,
+                                                                  int32_t* __restrict__ meta) {
+  __shared__ int64_t part[kSchedThreads];
+  __shared__ int64_t total_tiles, quantum, total_splits;
+  const int tid = threadIdx.x;
+  const int n = topk > 0 ? B * s_q : B;
+  int32_t* sched = meta + kMetaHeader;
+  int32_t* split_off = meta + meta_split_offset(W);
+  int32_t* first = meta + meta_tile_first(W, n);
+
+  const int per = (n + kSchedThreads - 1) / kSchedThreads;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+
+  // tile prefix sums
+  int64_t sum = 0;
+  for (int i = lo; i < hi; ++i) sum += stream_tiles(seqlens, topk, i);
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    const int64_t N = scan_parts(part);
+    int64_t q = (N + W - 1) / W;
+    if (q < min_tiles) q = min_tiles;
+    if (q < 1) q = 1;
+    total_tiles = N;
+    quantum = q;
+    first[n] = (int32_t)N;
+  }
+  __syncthreads();
+  {
+    int64_t acc = part[tid];
+    for (int i = lo; i < hi; ++i) {
+      first[i] = (int32_t)acc;
+      acc += stream_tiles(seqlens, topk, i);
+    }
+  }
+  const int64_t N = total_tiles, q = quantum;
+  __syncthreads();
+
+  // splits per stream = workers meeting it
+  sum = 0;
+  for (int i = lo; i < hi; ++i) {
+    const int64_t t = stream_tiles(seqlens, topk, i);
+    sum += t == 0 ? 0 : ((int64_t)first[i] + t - 1) / q - (int64_t)first[i] / q + 1;
+  }
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    total_splits = scan_parts(part);
+    split_off[n] = (int32_t)total_splits;
+  }
+  __syncthreads();
+  {
+    int64_t acc = part[tid];
+    for (int i = lo; i < hi; ++i) {
+      split_off[i] = (int32_t)acc;
+      const int64_t t = stream_tiles(seqlens, topk, i);
+      acc += t == 0 ? 0 : ((int64_t)first[i] + t - 1) / q - (int64_t)first[i] / q + 1;
+    }
+  }
+  __syncthreads();
+
+  // per-worker ranges
+  for (int w = tid; w < W; w += kSchedThreads) {
+    int32_t* e = sched + (int64_t)w * kSchedStride;
+    const int64_t wlo = (int64_t)w * q;
+    int64_t whi = (int64_t)(w + 1) * q;
+    if (whi > N) whi = N;
+    int32_t v[kSchedStride] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (wlo >= N) {
+      v[0] = v[2] = n;
+    } else {
+      const int bs = upper_bound(first, n + 1, wlo) - 1;
+      const int es = upper_bound(first + 1, n, whi);
+      v[0] = bs;
+      v[1] = (int32_t)(wlo - first[bs]);
+      v[2] = es;
+      v[3] = es < n ? (int32_t)(whi - first[es]) : 0;
+      v[4] = (int32_t)(split_off[bs] + (w - (int64_t)first[bs] / q));
+    }
+    for (int k = 0; k < kSchedStride; ++k) e[k] = v[k];
+  }
+  if (tid == 0) {
+    int32_t h[kMetaHeader] = {0};
+    h[MH_MAGIC] = kMetaMagic;
+    h[MH_NSTREAMS] = n;
+    h[MH_W] = W;
+    h[MH_Q] = (int32_t)q;
+    h[MH_N] = (int32_t)N;
+    h[MH_SPLITS] = (int32_t)total_splits;
+    h[MH_RSTREAM] = topk > 0 ? h_q : s_q * h_q;
+    h[MH_MINTILES] = min_tiles;
+    h[MH_TOPK] = topk;
+    h[MH_B] = B;
+    h[MH_SQ] = s_q;
+    h[MH_HQ] = h_q;
+    for (int k = 0; k < kMetaHeader; ++k) meta[k] = h[k];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sched(const int32_t* seqlens, int B, int s_q, int h_q, int topk, int W, int min_tiles, int32_t* meta,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(mla_sched_kernel, dim3(1), dim3(kSchedThreads), 0, stream, seqlens, B, s_q, h_q, topk, W, min_tiles,
+                     meta);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bit-exact: the FP8 -> bf16 decode, the metadata (against the oracle's plain
+schedule rule) and the page indirection (permuting pages gives identical
+bits).  Floating point: o within 8e-3 + 1e-2 |o_ref| elementwise, lse within
+1e-3, -inf / 0 exactly for empty attended sets.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+import oracle
+from gpu_helpers import DEV, check_problem, compare, flat, run_gpu, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import mla_paged_kv_get_amd as mla
+
+    mla.lib()
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+
+
+# --------------------------------------------------------------------------------------
+# bit-exact pieces
+
+
+def test_fp8_decode_bit_exact():
+    import mla_paged_kv_get_amd as mla
+
+    say("[gpu] fp8 decode: 256 codes x 12 scales")
+    scales = np.array([1.0, 0.0023, 3.7e-5, 448.0 / 7.0, 1.5e-38, 2.0 ** -120, 0.1, 7.0, 1e-3, 123.456, 2.0 ** -126,
+                       0.0], dtype=np.float32)
+    n = 256 * 3
+    tok = np.zeros((n, 656), dtype=np.uint8)
+    rng = np.random.default_rng(0)
+    for t in range(n):
+        tok[t, :512] = (np.arange(512) + t) % 256
+        tok[t, 512:528] = scales[(np.arange(4) + t) % len(scales)].view(np.uint8)
+        tok[t, 528:] = rng.integers(0, 256, 128, dtype=np.uint8)
+    got = mla.mla_debug_dequant_fp8(torch.from_numpy(tok).to(DEV)).cpu().view(torch.int16).numpy().view(np.uint16)
+    torch.cuda.synchronize()
+    for t in range(n):
+        sc = tok[t, 512:528].view(np.float32)
+        want = oracle.fp8_dequant_bf16(tok[t, :512], np.repeat(sc, 128))
+        nan = (tok[t, :512] & 0x7F) == 0x7F
+        g = got[t, :512]
+        assert np.array_equal(g[~nan], want[~nan]), "token %d" % t
+        assert np.all(((g[nan] & 0x7F80) == 0x7F80) & ((g[nan] & 0x7F) != 0))
+        assert np.array_equal(got[t, 512:], tok[t, 528:].view(np.uint16))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_metadata_matches_schedule_rule(seed):
+    import mla_paged_kv_get_amd as mla
+
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 50))
+    s_q = int(rng.integers(1, 3))
+    topk = int(rng.choice([0, 0, 64, 2048]))
+    seqlens = rng.integers(0, 9000, size=B).astype(np.int32)
+    seqlens[rng.random(B) < 0.2] = 0
+    W = int(rng.choice([1, 7, 64, 256, 1000]))
+    say("[gpu] metadata B=%d s_q=%d topk=%d W=%d" % (B, s_q, topk, W))
+    meta = mla.mla_get_metadata(torch.from_numpy(seqlens).to(DEV), s_q, 64, 1, topk, False, W)
+    m = meta.tensor.cpu().numpy()
+    torch.cuda.synchronize()
+    n_streams = B * s_q if topk else B
+    assert m[1] == n_streams and m[2] == W
+    sched_ref, off_ref = oracle.schedule(seqlens, s_q, topk, W, int(m[7]))
+    assert np.array_equal(m[16:16 + 8 * W].reshape(W, 8), sched_ref)
+    assert np.array_equal(m[16 + 8 * W:16 + 8 * W + n_streams + 1], off_ref)
+    assert m[5] == off_ref[-1]
+
+
+# --------------------------------------------------------------------------------------
+# small parity cases: several tiles, ragged tails, every variant
+
+
+SMALL = [
+    dict(name="dense bf16 h16 ragged", B=3, s_q=1, h_q=16, seqlens=[1, 200, 64], seed=1),
+    dict(name="dense bf16 h128", B=2, s_q=1, h_q=128, seqlens=[300, 1000], seed=2),
+    dict(name="dense bf16 s_q=2 h64 (128 rows)", B=2, s_q=2, h_q=64, seqlens=[513, 77], seed=3),
+    dict(name="dense bf16 s_q=2 h128 (256 rows)", B=2, s_q=2, h_q=128, seqlens=[700, 129], seed=4),
+    dict(name="dense fp8 h64", B=2, s_q=1, h_q=64, seqlens=[450, 65], seed=5, is_fp8=True),
+    dict(name="sparse bf16 h128", B=2, s_q=1, h_q=128, seqlens=[3000, 500], seed=6, topk=256, n_invalid=13),
+    dict(name="sparse fp8 h128", B=3, s_q=1, h_q=128, seqlens=[5000, 2500, 700], seed=7, topk=512, is_fp8=True,
+         n_invalid=25),
+    dict(name="sparse fp8 s_q=2 h64 clip", B=2, s_q=2, h_q=64, seqlens=[2000, 100], seed=8, topk=300, is_fp8=True,
+         recipe="clip"),
+    dict(name="sparse fp8 h16 topk 40", B=2, s_q=1, h_q=16, seqlens=[90, 60], seed=9, topk=40, is_fp8=True,
+         recipe="clip"),
+    dict(name="dense bf16 h96 (partial row tile)", B=2, s_q=1, h_q=96, seqlens=[333, 64], seed=10),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c["name"] for c in SMALL])
+def test_small_parity(case):
+    c = dict(case)
+    prob = mi.make_problem(c.pop("name"), **c)
+    check_problem(prob)
+
+
+@pytest.mark.parametrize("W", [1, 7, 256, 1000])
+def test_forced_worker_counts(W):
+    prob = mi.make_problem("dense bf16 splits", 3, 1, 64, [2000, 64, 700], seed=21)
+    check_problem(prob, num_workers=W, what="dense W=%d" % W)
+    sp = mi.make_problem("sparse fp8 splits", 2, 2, 64, [4000, 900], seed=22, topk=600, is_fp8=True, recipe="clip")
+    check_problem(sp, num_workers=W, what="sparse fp8 W=%d" % W)
+
+
+# --------------------------------------------------------------------------------------
+# edge cases
+
+
+def test_empty_streams_and_all_masked():
+    prob = mi.make_problem("dense with empty request", 3, 1, 16, [0, 100, 0], seed=31, max_blocks=2)
+    check_problem(prob, num_workers=5)
+    sp = mi.make_problem("sparse all -1", 2, 1, 64, [300, 300], seed=32, topk=128)
+    sp.indices[1] = -1
+    sp.indices[0, 0, 5:] = -1
+    check_problem(sp, num_workers=3)
+
+
+@pytest.mark.parametrize("is_fp8", [False, True])
+def test_single_token(is_fp8):
+    prob = mi.make_problem("single token", 1, 1, 64, [300], seed=41, topk=64, is_fp8=is_fp8)
+    prob.indices[0, 0] = -1
+    prob.indices[0, 0, 17] = 233
+    o, lse, _ = run_gpu(prob)
+    o, lse = flat(o, lse)
+    o_ref, lse_ref = oracle.problem_decode(prob)
+    assert np.array_equal(o, o_ref)  # p = 1: o is the token's V, bf16 exactly
+    compare(o, lse, o_ref, lse_ref, "single token")
+
+
+@pytest.mark.parametrize("is_fp8,topk", [(False, 0), (True, 0), (False, 200), (True, 200)])
+def test_unattended_nan_never_leaks(is_fp8, topk):
+    kw = dict(B=2, s_q=1, h_q=64, seqlens=[330, 100], seed=51, is_fp8=is_fp8, topk=topk, n_spare=3, max_blocks=8)
+    if topk:
+        kw.update(recipe="clip", n_invalid=10)
+    prob = mi.make_problem("nan-poisoned", nan_fill=True, **kw)
+    check_problem(prob, num_workers=4)
+
+
+def test_page_permutation_bit_identical():
+    prob = mi.make_problem("perm", 2, 1, 128, [900, 300], seed=61, n_spare=5)
+    o1, l1, _ = run_gpu(prob, 4)
+    g = torch.Generator().manual_seed(7)
+    perm = torch.randperm(prob.num_blocks, generator=g)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(perm.numel())
+    prob.kvcache = prob.kvcache[perm].contiguous()
+    prob.block_table = inv[prob.block_table.to(torch.int64)].to(torch.int32)
+    o2, l2, _ = run_gpu(prob, 4)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_dense_equals_sparse_full_list():
+    dense = mi.make_problem("d", 2, 1, 64, [150, 64], seed=71)
+    sparse = mi.make_problem("d", 2, 1, 64, [150, 64], seed=71)
+    idx = torch.full((2, 1, 192), -1, dtype=torch.int32)
+    for b, L in enumerate([150, 64]):
+        idx[b, :, :L] = torch.arange(L, dtype=torch.int32)
+    sparse.indices = idx
+    od, ld, _ = run_gpu(dense, 2)
+    os_, ls, _ = run_gpu(sparse, 2)
+    o, lse = flat(od, ld)
+    o2, lse2 = flat(os_, ls)
+    o_ref, lse_ref = oracle.problem_decode(dense)
+    compare(o, lse, o_ref, lse_ref, "dense")
+    compare(o2, lse2, o_ref, lse_ref, "sparse as dense")
+
+
+def test_deterministic():
+    prob = mi.make_problem("det", 4, 1, 128, [1500, 20, 800, 64], seed=81, is_fp8=True, topk=256, n_invalid=9,
+                           recipe="clip")
+    d = to_device(prob)
+    o1, l1, m = run_gpu(prob, dev_inputs=d)
+    o2, l2, _ = run_gpu(prob, dev_inputs=d, meta=m)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_lse_merge_through_the_abi():
+    """Two calls over the two halves of each index list, merged with the oracle's
+    lse rule, equal one call over the whole list."""
+    prob = mi.make_problem("halves", 2, 1, 64, [3000, 3000], seed=91, topk=512, is_fp8=True, n_invalid=30)
+    o, lse, _ = run_gpu(prob)
+    o, lse = flat(o, lse)
+    parts = []
+    for half in range(2):
+        p2 = mi.make_problem("halves", 2, 1, 64, [3000, 3000], seed=91, topk=512, is_fp8=True, n_invalid=30)
+        p2.indices = p2.indices.clone()
+        p2.indices[:, :, half * 256:(half + 1) * 256] = -1
+        oh, lh, _ = run_gpu(p2)
+        parts.append(flat(oh, lh))
+    merged_o = np.zeros_like(o)
+    merged_l = np.zeros_like(lse)
+    for r in range(o.shape[0]):
+        mo, ml = oracle.lse_combine(np.stack([parts[0][0][r], parts[1][0][r]]), np.array([parts[0][1][r], parts[1][1][r]]))
+        merged_o[r], merged_l[r] = mo, ml
+    o_ref, lse_ref = oracle.problem_decode(prob)
+    compare(merged_o, merged_l, o_ref, lse_ref, "merged halves")
+    compare(o, lse, o_ref, lse_ref, "whole")
