@@ -42,6 +42,20 @@ __device__ __attribute__((aligned(64))) uint8_t g_zero_token[kBf16TokenBytes] = 
 
 namespace {
 
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() implies a
+// release fence that also waits for every outstanding global->LDS load, which
+// would drain the tiles streaming ahead; these barriers leave them in flight.
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Also wait until at most 9 (one sub-tile's worth of) global->LDS loads of this
+// wave are outstanding, i.e. the previous sub-tile has landed.
+__device__ __forceinline__ void tile_barrier_keep9() {
+  asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void tile_barrier_drain() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kSub = 32;                               // tokens per sub-tile
@@ -240,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       MLA_LDS f32x4* xp = (MLA_LDS f32x4*)(xbuf + (((u & 1) * 4 + partner) * 64 + lane) * 16);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) xo[q4] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-      __syncthreads();
+      lds_barrier();
       float x[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -346,13 +360,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       compute(u, buffer(u));
       if (FP8 && u + 1 < u1) store_fp8(next, buffer(u + 1));
       if (SPARSE && wave == 0) publish(u + 3, tok_pref);
-      if (!FP8) {
-        if (u + 2 < u1)
-          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // u + 1 landed, u + 2 may fly
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      __syncthreads();
+      if (FP8)
+        lds_barrier();  // sub-tile u + 1 went through registers; u + 2 stays in flight
+      else if (u + 2 < u1)
+        tile_barrier_keep9();  // u + 1 landed, u + 2 may still fly
+      else
+        tile_barrier_drain();
     };
     for (int u = u0; u < u1; u += 2) {
       step(u, rawA, rawB);

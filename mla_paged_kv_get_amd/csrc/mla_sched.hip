@@ -11,7 +11,9 @@
 //   worker w owns global tiles [w q, min((w + 1) q, N)) of the streams laid end
 //   to end; each stream's splits are the workers that meet it, in worker order.
 // One workgroup of 256 threads: chunked prefix sums over the streams, then one
-// binary search per worker.
+// binary search per worker.  Up to kLdsStreams streams the prefix arrays live in
+// LDS (the searches then cost no global round trips); beyond that they are
+// built in place in the metadata buffer.
 #include "mla_common.hpp"
 
 namespace mla {
@@ -19,6 +21,7 @@ namespace mla {
 namespace {
 
 constexpr int kSchedThreads = 256;
+constexpr int kLdsStreams = 8192;
 
 __device__ __forceinline__ int64_t stream_tiles(const int32_t* seqlens, int topk, int i) {
   const int64_t len = topk > 0 ? (int64_t)topk : (int64_t)seqlens[i];
@@ -54,11 +57,15 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t*
                                                                   int32_t* __restrict__ meta) {
   __shared__ int64_t part[kSchedThreads];
   __shared__ int64_t total_tiles, quantum, total_splits;
+  __shared__ int32_t lds_first[kLdsStreams + 1], lds_split[kLdsStreams + 1];
   const int tid = threadIdx.x;
   const int n = topk > 0 ? B * s_q : B;
   int32_t* sched = meta + kMetaHeader;
-  int32_t* split_off = meta + meta_split_offset(W);
-  int32_t* first = meta + meta_tile_first(W, n);
+  int32_t* g_split = meta + meta_split_offset(W);
+  int32_t* g_first = meta + meta_tile_first(W, n);
+  const bool in_lds = n <= kLdsStreams;
+  int32_t* split_off = in_lds ? (int32_t*)lds_split : g_split;
+  int32_t* first = in_lds ? (int32_t*)lds_first : g_first;
 
   const int per = (n + kSchedThreads - 1) / kSchedThreads;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
@@ -131,6 +138,11 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t*
     }
     for (int k = 0; k < kSchedStride; ++k) e[k] = v[k];
   }
+  if (in_lds)
+    for (int i = tid; i <= n; i += kSchedThreads) {
+      g_first[i] = first[i];
+      g_split[i] = split_off[i];
+    }
   if (tid == 0) {
     int32_t h[kMetaHeader] = {0};
     h[MH_MAGIC] = kMetaMagic;
