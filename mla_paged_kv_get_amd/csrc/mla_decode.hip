@@ -23,10 +23,10 @@
 //      v_mfma_f32_32x32x16_bf16 (the K tile is the A operand), the pair swaps the
 //      partials through LDS and both add them in the same order, so both hold the
 //      same scores;
-//   3. online softmax in the log2 domain, lane-local (S^T puts query row
-//      lane % 32 in every lane's accumulator column) with a lazy reference
-//      maximum: the accumulators are rescaled only when a row maximum grows by
-//      more than 2^8, which keeps P <= 256 and makes rescales rare;
+//   3. softmax in the log2 domain, lane-local (S^T puts query row lane % 32 in
+//      every lane's accumulator column) against a per-row reference fixed at the
+//      first scores of the split (see the main loop), so O and l need no
+//      rescaling and O is touched only by MFMAs;
 //   4. O^T += V^T P^T on the same MFMA: P goes from the score registers straight
 //      into the B operand, V^T comes from the token-major tile through
 //      ds_read_b64_tr_b16.
@@ -57,15 +57,17 @@ __device__ __forceinline__ void tile_barrier_drain() {
 }
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kRescaleLog2 = 8.0f;
+constexpr float kRefLift = 32.0f;   // log2 units
+constexpr float kRefRoom = 88.0f;
 constexpr int kSub = 32;                               // tokens per sub-tile
 constexpr int kSubBytes = kSub * kBf16TokenBytes;      // 36864
 constexpr int kNBuf = 3;
-constexpr int kXOffset = kNBuf * kSubBytes;            // S exchange: [2][4 waves][64 lanes][16 f32]
+constexpr int kXOffset = kNBuf * kSubBytes;            // S exchange: [2][4 waves][4][64 lanes] f32x4
 constexpr int kXBytes = 4 * 64 * 16 * 4;
 constexpr int kTokOffset = kXOffset + 2 * kXBytes;     // int32 tokidx[4][32]
 constexpr int kMaskOffset = kTokOffset + 4 * kSub * 4;  // uint32 vmask[4]
-constexpr int kLdsBytes = kMaskOffset + 4 * 4;
+constexpr int kFlagOffset = kMaskOffset + 4 * 4;        // int32 per-wave flags[4]
+constexpr int kLdsBytes = kFlagOffset + 4 * 4;
 constexpr int kBf16LoadsPerThread = kSubBytes / 16 / kThreads;  // 9
 
 // FP8 registers of one sub-tile for this thread: token tid / 8, code chunks
@@ -81,9 +83,10 @@ template <bool FP8, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
-  MLA_LDS float* xbuf = (MLA_LDS float*)(smem + kXOffset);
+  MLA_LDS f32x4* xbuf = (MLA_LDS f32x4*)(smem + kXOffset);
   MLA_LDS int32_t* tokidx = (MLA_LDS int32_t*)(smem + kTokOffset);
   MLA_LDS uint32_t* vmask = (MLA_LDS uint32_t*)(smem + kMaskOffset);
+  MLA_LDS int32_t* wflag = (MLA_LDS int32_t*)(smem + kFlagOffset);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -114,9 +117,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   const int bs = ent[0], bt0 = ent[1], es = ent[2], et = ent[3], split0 = ent[4];
   const int32_t* split_off = p.meta + meta_split_offset(p.W);
   const int32_t* first = p.meta + meta_tile_first(p.W, p.n_streams);
-  const int tok_bytes = FP8 ? kFp8TokenBytes : kBf16TokenBytes;
+  constexpr int tok_bytes = FP8 ? kFp8TokenBytes : kBf16TokenBytes;
 
-  // ---- per-lane LDS offsets (independent of the sub-tile) ---------------------
+  // ---- per-lane constants -------------------------------------------------------
   // K operand: token l32, chunk c(kk) = 32 hf + 2 kk + h for kk < 16, and
   // 64 + 4 hf + 2 (kk - 16) + h for kk = 16, 17.
   const int ksw = tile_swizzle(l32);
@@ -142,6 +145,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
         vofs[s2][e4][1] = base - 64 * sb;
       }
   }
+  // BF16 staging: load k of this thread fills LDS slot s = (9 wave + k) 64 + lane,
+  // i.e. token dtok[k] of the sub-tile, source chunk dchunk[k]
+  int dtok[kBf16LoadsPerThread], dchunk[kBf16LoadsPerThread];
+#pragma unroll
+  for (int k = 0; k < kBf16LoadsPerThread; ++k) {
+    const int s = (wave * kBf16LoadsPerThread + k) * 64 + lane;
+    dtok[k] = s / kTokenChunks;
+    dchunk[k] = (s - dtok[k] * kTokenChunks) ^ tile_swizzle(dtok[k]);
+  }
+  // exchange slots of this lane: [(u & 1)][wave][q4][lane]
+  const int xo_base = wave * 4 * 64 + lane, xp_base = partner * 4 * 64 + lane;
 
   for (int stream = bs; stream <= es && stream < p.n_streams; ++stream) {
     const int ntiles = first[stream + 1] - first[stream];
@@ -178,13 +192,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     }
 
     f32x16 acc[8];
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[cb][e] = 0.f;
-    float m_ref = kNegInf, l_sum = 0.f;
 
-    // ---- sparse index pipeline (wave 0, lanes 0..31) -----------------------------
+    // ---- sparse index pipeline (wave 0) -------------------------------------------
     auto idx_at = [&](int u) -> int {
       const int slot = u * kSub + l32;
       return (u < u1 && slot < p.topk) ? idx_row[slot] : -1;
@@ -195,8 +204,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       if (lane < kSub) tokidx[(u & 3) * kSub + lane] = tok;
       if (lane == 0) vmask[u & 3] = (uint32_t)m;
     };
-    // ---- staging of sub-tile u into buffer `buf` -------------------------------
-    // page: the cache page of sub-tile u (dense; prefetched by the caller)
+    // ---- staging ------------------------------------------------------------------
+    auto page_of = [&](int u) -> int { return (!SPARSE && u < u1) ? bt_row[u >> 1] : 0; };
+    auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((u - u0) % kNBuf) * kSubBytes; };
+    // byte address of stored token t of sub-tile u (the zero token when not attended)
     auto token_ptr = [&](int u, int t, int page) -> const uint8_t* {
       if (SPARSE) {
         const int tok = tokidx[(u & 3) * kSub + t];
@@ -206,14 +217,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       return p.kv + ((int64_t)page * kPage + (u & 1) * kSub + t) * tok_bytes;
     };
     auto stage_bf16 = [&](int u, int page, MLA_LDS char* buf) {
+      if (!SPARSE && (u + 1) * kSub <= seqlen) {
+        // full dense sub-tile: one uniform base, per-lane 32-bit offsets
+        const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
 #pragma unroll
-      for (int k = 0; k < kBf16LoadsPerThread; ++k) {
-        const int inst = wave * kBf16LoadsPerThread + k;
-        const int s = inst * 64 + lane;
-        const int t = s / kTokenChunks;
-        const int c = (s - t * kTokenChunks) ^ tile_swizzle(t);
-        __builtin_amdgcn_global_load_lds((const void*)(token_ptr(u, t, page) + c * 16),
-                                         (MLA_LDS void*)(buf + inst * 1024), 16, 0, 0);
+        for (int k = 0; k < kBf16LoadsPerThread; ++k)
+          __builtin_amdgcn_global_load_lds((const void*)(base + dtok[k] * kBf16TokenBytes + dchunk[k] * 16),
+                                           (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024), 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kBf16LoadsPerThread; ++k)
+          __builtin_amdgcn_global_load_lds((const void*)(token_ptr(u, dtok[k], page) + dchunk[k] * 16),
+                                           (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024), 16, 0, 0);
       }
     };
     auto load_fp8 = [&](int u, int page, RawFp8& r) {
@@ -236,11 +251,71 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       }
       *(MLA_LDS u32x4*)(buf + tile_slot(t, 64 + j) * 16) = r.r;
     };
-    auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((u - u0) % kNBuf) * kSubBytes; };
-    auto page_of = [&](int u) -> int { return (!SPARSE && u < u1) ? bt_row[u >> 1] : 0; };
 
-    // ---- one sub-tile of compute ------------------------------------------------
-    auto compute = [&](int u, MLA_LDS char* buf) {
+    // Reference maximum m_ref (log2 domain, per row): the row's first finite
+    // sub-tile maximum + kRefLift, fixed for the whole split, so P = 2^(x - m_ref)
+    // stays within [2^-126, 2^(kRefLift + kRefRoom)] for every score within
+    // (kRefRoom, 126 - kRefLift) of that first maximum, and O changes only through
+    // MFMAs.  A score more than kRefRoom above m_ref (scores spread by over ~60
+    // natural-log units) marks the pass as overflowed and the split is recomputed
+    // from the start with the split's true maximum as the reference.
+    float m_ref = kNegInf, m_seen = kNegInf, l_sum = 0.f;
+    bool redo = false;
+    do {
+    l_sum = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[cb][e] = 0.f;
+    if (redo) m_ref = m_seen + kRefLift;
+    bool overflow = false;
+
+    // ---- prologue: index data for u0 .. u0 + 2, stage u0 (and u0 + 1) --------------
+    int idx_pref = -1;  // sparse: index of slot l32 of sub-tile u + 3 (wave 0)
+    if (SPARSE) {
+      if (wave == 0) {
+        publish(u0, tok_of(idx_at(u0)));
+        publish(u0 + 1, tok_of(idx_at(u0 + 1)));
+        publish(u0 + 2, tok_of(idx_at(u0 + 2)));
+        idx_pref = idx_at(u0 + 3);
+      }
+      __syncthreads();
+    }
+    RawFp8 raw;  // FP8: sub-tile u + 1 in flight in VGPRs
+    if (FP8) {
+      load_fp8(u0, page_of(u0), raw);
+      store_fp8(raw, buffer(u0));
+      if (u0 + 1 < u1) load_fp8(u0 + 1, page_of(u0 + 1), raw);
+    } else {
+      stage_bf16(u0, page_of(u0), buffer(u0));
+      if (u0 + 1 < u1) {
+        stage_bf16(u0 + 1, page_of(u0 + 1), buffer(u0 + 1));
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // sub-tile u0 has landed
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    }
+    int page_pref = page_of(u0 + 2);  // dense: page of sub-tile u + 2
+    __syncthreads();
+
+    // ---- per sub-tile: part 1 (staging ahead, scores, max) --------------------------
+    float x[16];
+    int tok_pref = -1;
+    auto part1 = [&](int u) -> float {
+      MLA_LDS char* buf = buffer(u);
+      if (SPARSE && wave == 0) {
+        tok_pref = tok_of(idx_pref);  // sub-tile u + 3; its index came last round
+        idx_pref = idx_at(u + 4);
+      }
+      const int page2 = page_pref;
+      page_pref = page_of(u + 3);
+      __builtin_amdgcn_sched_barrier(0);  // index loads stay ahead of the tile loads
+      if (FP8) {
+        if (u + 1 < u1) store_fp8(raw, buffer(u + 1));  // arrived during the last round
+        if (u + 2 < u1) load_fp8(u + 2, page2, raw);
+      } else if (u + 2 < u1) {
+        stage_bf16(u + 2, page2, buffer(u + 2));
+      }
       // partial S^T over this wave's dims
       f32x16 s = {};
 #pragma unroll
@@ -250,53 +325,47 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
       }
       // swap partial scores with the partner wave
-      MLA_LDS f32x4* xo = (MLA_LDS f32x4*)(xbuf + (((u & 1) * 4 + wave) * 64 + lane) * 16);
-      MLA_LDS f32x4* xp = (MLA_LDS f32x4*)(xbuf + (((u & 1) * 4 + partner) * 64 + lane) * 16);
+      MLA_LDS f32x4* xo = xbuf + (u & 1) * (4 * 4 * 64) + xo_base;
+      MLA_LDS f32x4* xp = xbuf + (u & 1) * (4 * 4 * 64) + xp_base;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) xo[q4] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+      for (int q4 = 0; q4 < 4; ++q4) xo[q4 * 64] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
       lds_barrier();
-      float x[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 o = xp[q4];
+        const f32x4 o = xp[q4 * 64];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // both waves add (hf 0 partial) + (hf 1 partial)
           const float mine = s[4 * q4 + e], theirs = o[e];
-          x[4 * q4 + e] = hf == 0 ? mine + theirs : theirs + mine;
+          x[4 * q4 + e] = (hf == 0 ? mine + theirs : theirs + mine) * p.scale_log2;
         }
       }
-      // mask and scale: lane holds row l32, tokens 8 (e / 4) + 4 h + e % 4
-      const uint32_t tmask = SPARSE ? vmask[u & 3] : 0u;
-      const int vcount = SPARSE ? kSub : seqlen - u * kSub;
-      float mx = kNegInf;
+      // mask: lane holds row l32, tokens 8 (e / 4) + 4 h + e % 4
+      const bool full = SPARSE ? vmask[u & 3] == 0xFFFFFFFFu : (u + 1) * kSub <= seqlen;
+      if (!full) {
+        const uint32_t tmask = SPARSE ? vmask[u & 3] : 0u;
+        const int vcount = seqlen - u * kSub;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tok = 8 * (e >> 2) + 4 * h + (e & 3);
-        const bool ok = SPARSE ? ((tmask >> tok) & 1u) != 0 : tok < vcount;
-        x[e] = ok ? x[e] * p.scale_log2 : kNegInf;
-        mx = fmaxf(mx, x[e]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_ref, mx);
-      const bool need = m_new > m_ref + kRescaleLog2;  // true on the first finite score too
-      if (__ballot(need) != 0) {
-        const float alpha = need ? (m_ref == kNegInf ? 0.f : exp2f(m_ref - m_new)) : 1.f;
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[cb][e] *= alpha;
+        for (int e = 0; e < 16; ++e) {
+          const int tok = 8 * (e >> 2) + 4 * h + (e & 3);
+          const bool ok = SPARSE ? ((tmask >> tok) & 1u) != 0 : tok < vcount;
+          x[e] = ok ? x[e] : kNegInf;
         }
-        l_sum *= alpha;
-        m_ref = need ? m_new : m_ref;
       }
+      float mx = x[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
+      return fmaxf(mx, __shfl_xor(mx, 32));
+    };
+    // ---- part 2 (probabilities, O^T += V^T P^T, hand over to the next sub-tile) ----
+    auto part2 = [&](int u) {
+      MLA_LDS char* buf = buffer(u);
       const float msafe = m_ref == kNegInf ? 0.f : m_ref;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        x[e] = exp2f(x[e] - msafe);
+        x[e] = __builtin_amdgcn_exp2f(x[e] - msafe);
         l_sum += x[e];
       }
-      // O^T += V^T P^T over two 16-token k-steps
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8 pb;
@@ -310,55 +379,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
           acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[cb], 0, 0, 0);
         }
       }
-    };
-
-    // ---- prologue: index data for u0 .. u0 + 2, stage u0 and u0 + 1 -------------
-    int idx_pref = -1;  // sparse: index of slot l32 of sub-tile u + 3 (wave 0)
-    if (SPARSE) {
-      if (wave == 0) {
-        publish(u0, tok_of(idx_at(u0)));
-        publish(u0 + 1, tok_of(idx_at(u0 + 1)));
-        publish(u0 + 2, tok_of(idx_at(u0 + 2)));
-        idx_pref = idx_at(u0 + 3);
-      }
-      __syncthreads();
-    }
-    RawFp8 rawA, rawB;  // FP8: the next two sub-tiles in flight in VGPRs
-    if (FP8) {
-      load_fp8(u0, page_of(u0), rawA);
-      store_fp8(rawA, buffer(u0));
-      if (u0 + 1 < u1) load_fp8(u0 + 1, page_of(u0 + 1), rawA);
-    } else {
-      stage_bf16(u0, page_of(u0), buffer(u0));
-      if (u0 + 1 < u1) {
-        stage_bf16(u0 + 1, page_of(u0 + 1), buffer(u0 + 1));
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // sub-tile u0 has landed
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-    }
-    int page_pref = page_of(u0 + 2);  // dense: page of sub-tile u + 2
-    __syncthreads();
-
-    // ---- main loop: compute u while u + 1 and u + 2 stream in ---------------------
-    // next: registers holding sub-tile u + 1 (FP8); fill: receives sub-tile u + 2
-    auto step = [&](int u, RawFp8& next, RawFp8& fill) {
-      int tok_pref = -1;
-      if (SPARSE && wave == 0) {
-        tok_pref = tok_of(idx_pref);  // sub-tile u + 3; its index came last round
-        idx_pref = idx_at(u + 4);
-      }
-      const int page2 = page_pref;
-      page_pref = page_of(u + 3);
-      __builtin_amdgcn_sched_barrier(0);  // index loads stay ahead of the tile loads
-      if (u + 2 < u1) {
-        if (FP8)
-          load_fp8(u + 2, page2, fill);
-        else
-          stage_bf16(u + 2, page2, buffer(u + 2));
-      }
-      compute(u, buffer(u));
-      if (FP8 && u + 1 < u1) store_fp8(next, buffer(u + 1));
       if (SPARSE && wave == 0) publish(u + 3, tok_pref);
       if (FP8)
         lds_barrier();  // sub-tile u + 1 went through registers; u + 2 stays in flight
@@ -367,10 +387,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       else
         tile_barrier_drain();
     };
-    for (int u = u0; u < u1; u += 2) {
-      step(u, rawA, rawB);
-      if (u + 1 < u1) step(u + 1, rawB, rawA);
+
+    // ---- main loop ---------------------------------------------------------------------
+    for (int u = u0; u < u1; ++u) {
+      const float mx = part1(u);
+      m_seen = fmaxf(m_seen, mx);
+      if (m_ref == kNegInf && mx != kNegInf) m_ref = mx + kRefLift;
+      overflow |= mx > m_ref + kRefRoom;
+      part2(u);
     }
+    // the restart must be taken by the whole workgroup (it contains barriers)
+    if (lane == 0) wflag[wave] = __ballot(overflow) != 0 ? 1 : 0;
+    __syncthreads();
+    redo = (wflag[0] | wflag[1] | wflag[2] | wflag[3]) != 0;
+    __syncthreads();
+    } while (redo);
 
     // ---- epilogue -------------------------------------------------------------------
     l_sum += __shfl_xor(l_sum, 32);
