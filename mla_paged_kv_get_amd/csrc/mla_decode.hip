@@ -47,10 +47,15 @@ namespace {
 // would drain the tiles streaming ahead; these barriers leave them in flight.
 // The memory clobber keeps the compiler from moving memory accesses across.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Also wait until at most 9 (one sub-tile's worth of) global->LDS loads of this
-// wave are outstanding, i.e. the previous sub-tile has landed.
-__device__ __forceinline__ void tile_barrier_keep9() {
-  asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Also wait until at most N global->LDS loads of this wave are outstanding:
+// with N = the loads one round issues, everything issued before this round has
+// landed (the hardware completes these loads in order).
+template <int N>
+__device__ __forceinline__ void tile_barrier_keep() {
+  static_assert(N == 9 || N == 10 || N == 11, "unexpected load count");
+  if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (N == 11) asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ void tile_barrier_drain() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -64,9 +69,12 @@ constexpr int kSubBytes = kSub * kBf16TokenBytes;      // 36864
 constexpr int kNBuf = 3;
 constexpr int kXOffset = kNBuf * kSubBytes;            // S exchange: [2][4 waves][4][64 lanes] f32x4
 constexpr int kXBytes = 4 * 64 * 16 * 4;
-constexpr int kTokOffset = kXOffset + 2 * kXBytes;     // int32 tokidx[4][32]
-constexpr int kMaskOffset = kTokOffset + 4 * kSub * 4;  // uint32 vmask[4]
-constexpr int kFlagOffset = kMaskOffset + 4 * 4;        // int32 per-wave flags[4]
+// Metadata: BF16 rings int32 ring_idx[8][64], ring_pg[8][64]; FP8 int32
+// tokidx[4][32] and uint32 vmask[4] in the same space.
+constexpr int kRing = 8;
+constexpr int kMetaOffset = kXOffset + 2 * kXBytes;
+constexpr int kMetaBytes = 2 * kRing * 64 * 4;
+constexpr int kFlagOffset = kMetaOffset + kMetaBytes;  // int32 per-wave flags[4]
 constexpr int kLdsBytes = kFlagOffset + 4 * 4;
 constexpr int kBf16LoadsPerThread = kSubBytes / 16 / kThreads;  // 9
 
@@ -84,8 +92,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   MLA_LDS f32x4* xbuf = (MLA_LDS f32x4*)(smem + kXOffset);
-  MLA_LDS int32_t* tokidx = (MLA_LDS int32_t*)(smem + kTokOffset);
-  MLA_LDS uint32_t* vmask = (MLA_LDS uint32_t*)(smem + kMaskOffset);
+  MLA_LDS int32_t* ring_idx = (MLA_LDS int32_t*)(smem + kMetaOffset);
+  MLA_LDS int32_t* ring_pg = ring_idx + kRing * 64;
+  MLA_LDS int32_t* tokidx = (MLA_LDS int32_t*)(smem + kMetaOffset);
+  MLA_LDS uint32_t* vmask = (MLA_LDS uint32_t*)(tokidx + 4 * kSub);
   MLA_LDS int32_t* wflag = (MLA_LDS int32_t*)(smem + kFlagOffset);
 
   const int tid = threadIdx.x;
@@ -147,12 +157,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   }
   // BF16 staging: load k of this thread fills LDS slot s = (9 wave + k) 64 + lane,
   // i.e. token dtok[k] of the sub-tile, source chunk dchunk[k]
+  // (byte offset doff[k] = dtok[k] * 1152 + 16 * source chunk within the sub-tile)
   int dtok[kBf16LoadsPerThread], dchunk[kBf16LoadsPerThread];
+  uint32_t doff[kBf16LoadsPerThread];
 #pragma unroll
   for (int k = 0; k < kBf16LoadsPerThread; ++k) {
     const int s = (wave * kBf16LoadsPerThread + k) * 64 + lane;
     dtok[k] = s / kTokenChunks;
     dchunk[k] = (s - dtok[k] * kTokenChunks) ^ tile_swizzle(dtok[k]);
+    doff[k] = (uint32_t)(dtok[k] * kBf16TokenBytes + dchunk[k] * 16);
   }
   // exchange slots of this lane: [(u & 1)][wave][q4][lane]
   const int xo_base = wave * 4 * 64 + lane, xp_base = partner * 4 * 64 + lane;
@@ -193,47 +206,139 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
 
     f32x16 acc[8];
 
-    // ---- sparse index pipeline (wave 0) -------------------------------------------
-    auto idx_at = [&](int u) -> int {
-      const int slot = u * kSub + l32;
-      return (u < u1 && slot < p.topk) ? idx_row[slot] : -1;
+    // ---- per sub-tile metadata ----------------------------------------------------
+    // Whatever a round needs to know about a later sub-tile (its cache page, or
+    // the token rows of its 32 index slots) is fetched rounds ahead into LDS, so
+    // no round waits on a global load it has just issued.
+    //
+    // BF16 (tiles arrive by direct global->LDS loads): the metadata travels the
+    // same way, into rings of 8 sub-tiles.  Round u fetches the page of sub-tile
+    // u + 4 (dense) or the indices of sub-tile u + 6 and the pages of sub-tile
+    // u + 4's indices (sparse).  A direct load issued in round r has landed once
+    // round r + 1 ends, so every wave sees it from round r + 2 on; round u stages
+    // sub-tile u + 2.  No loaded value ever lands in a register here: the
+    // compiler could only wait for such a value by draining every direct load
+    // still streaming.
+    //
+    // FP8 (tiles go through registers): sub-tile u's metadata sits in LDS slot
+    // u & 3 (dense: its page; sparse: the token row of each slot, -1 when not
+    // attended, and the attended mask); every wave loads the metadata of sub-tile
+    // u + 3 during round u and wave 0 publishes it at the end of the round.
+    auto slot_ok = [&](int u) { return u < u1 && u * kSub + l32 < p.topk; };  // sparse slot l32 exists
+    // BF16 direct metadata loads (64 lanes each; lanes 32..63 repeat 0..31)
+    auto meta_dma = [&](int u) {
+      if constexpr (SPARSE) {
+        // indices of sub-tile u + 6
+        const int si = min((u + 6) * kSub + l32, p.topk - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(idx_row + si),
+                                         (MLA_LDS void*)(ring_idx + ((u + 6) & (kRing - 1)) * 64), 4, 0, 0);
+        // pages of sub-tile u + 4's indices
+        const int idx = ring_idx[((u + 4) & (kRing - 1)) * 64 + l32];
+        const bool ok = slot_ok(u + 4) && idx >= 0;
+        __builtin_amdgcn_global_load_lds((const void*)(bt_row + (ok ? idx >> 6 : 0)),
+                                         (MLA_LDS void*)(ring_pg + ((u + 4) & (kRing - 1)) * 64), 4, 0, 0);
+      } else {
+        // page of sub-tile u + 4 (the split's last page past its end)
+        __builtin_amdgcn_global_load_lds((const void*)(bt_row + (min(u + 4, u1 - 1) >> 1)),
+                                         (MLA_LDS void*)(ring_pg + ((u + 4) & (kRing - 1)) * 64), 4, 0, 0);
+      }
     };
-    auto tok_of = [&](int idx) -> int { return idx >= 0 ? bt_row[idx >> 6] * kPage + (idx & 63) : -1; };
-    auto publish = [&](int u, int tok) {
-      const uint64_t m = __ballot(tok >= 0);
-      if (lane < kSub) tokidx[(u & 3) * kSub + lane] = tok;
-      if (lane == 0) vmask[u & 3] = (uint32_t)m;
+    // BF16 prologue: the same ring entries by plain loads (rings for u0 .. u0 + 5)
+    auto meta_fill = [&]() {
+      if (wave == 0) {
+        if constexpr (SPARSE) {
+#pragma unroll
+          for (int j = 0; j < 6; ++j) {
+            const int u = u0 + j;
+            const int idx = idx_row[min(u * kSub + l32, p.topk - 1)];
+            ring_idx[(u & (kRing - 1)) * 64 + lane] = idx;
+            if (j < 4) {
+              const bool ok = slot_ok(u) && idx >= 0;
+              ring_pg[(u & (kRing - 1)) * 64 + lane] = bt_row[ok ? idx >> 6 : 0];
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int u = u0 + j;
+            ring_pg[(u & (kRing - 1)) * 64 + lane] = bt_row[min(u, u1 - 1) >> 1];
+          }
+        }
+      }
+    };
+    // FP8 metadata (plain loads)
+    auto idx_at = [&](int u) -> int { return slot_ok(u) ? idx_row[u * kSub + l32] : -1; };
+    auto tok_of = [&](int idx) -> int {
+      const int pg = bt_row[(idx < 0 ? 0 : idx) >> 6];  // always issued
+      return idx >= 0 ? pg * kPage + (idx & 63) : -1;
+    };
+    auto page_load = [&](int u) -> int { return bt_row[min(u, u1 - 1) >> 1]; };
+    auto publish = [&](int u, int v) {  // wave 0
+      if (SPARSE) {
+        const uint64_t m = __ballot(v >= 0);
+        if (lane < kSub) tokidx[(u & 3) * kSub + lane] = v;
+        if (lane == 0) vmask[u & 3] = (uint32_t)m;
+      } else if (lane == 0) {
+        tokidx[(u & 3) * kSub] = v;
+      }
+    };
+    // attended mask of sub-tile u's 32 slots (sparse)
+    auto sparse_mask = [&](int u) -> uint32_t {
+      if constexpr (FP8) {
+        return vmask[u & 3];
+      } else {
+        const bool ok = slot_ok(u) && ring_idx[(u & (kRing - 1)) * 64 + l32] >= 0;
+        return (uint32_t)__ballot(ok);
+      }
     };
     // ---- staging ------------------------------------------------------------------
-    auto page_of = [&](int u) -> int { return (!SPARSE && u < u1) ? bt_row[u >> 1] : 0; };
     auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((u - u0) % kNBuf) * kSubBytes; };
-    // byte address of stored token t of sub-tile u (the zero token when not attended)
-    auto token_ptr = [&](int u, int t, int page) -> const uint8_t* {
+    // FP8: byte address of stored token t of sub-tile u (the zero token when not attended)
+    auto token_ptr = [&](int u, int t) -> const uint8_t* {
       if (SPARSE) {
         const int tok = tokidx[(u & 3) * kSub + t];
         return tok >= 0 ? p.kv + (int64_t)tok * tok_bytes : g_zero_token;
       }
       if (u * kSub + t >= seqlen) return g_zero_token;
+      const int page = tokidx[(u & 3) * kSub];
       return p.kv + ((int64_t)page * kPage + (u & 1) * kSub + t) * tok_bytes;
     };
-    auto stage_bf16 = [&](int u, int page, MLA_LDS char* buf) {
-      if (!SPARSE && (u + 1) * kSub <= seqlen) {
-        // full dense sub-tile: one uniform base, per-lane 32-bit offsets
-        const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
+    auto stage_bf16 = [&](int u, MLA_LDS char* buf) {
+      const int r = (u & (kRing - 1)) * 64;
+      if constexpr (SPARSE) {
+        // token row of slot l32, then of each load's token
+        const int idx = ring_idx[r + l32];
+        const int pg = ring_pg[r + l32];
+        const int tok = (slot_ok(u) && idx >= 0) ? pg * kPage + (idx & 63) : -1;
 #pragma unroll
-        for (int k = 0; k < kBf16LoadsPerThread; ++k)
-          __builtin_amdgcn_global_load_lds((const void*)(base + dtok[k] * kBf16TokenBytes + dchunk[k] * 16),
+        for (int k = 0; k < kBf16LoadsPerThread; ++k) {
+          const int tk = __shfl(tok, dtok[k]);
+          const uint8_t* src = tk >= 0 ? p.kv + (int64_t)tk * kBf16TokenBytes : g_zero_token;
+          __builtin_amdgcn_global_load_lds((const void*)(src + dchunk[k] * 16),
                                            (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024), 16, 0, 0);
+        }
       } else {
+        const int page = __builtin_amdgcn_readfirstlane(ring_pg[r]);
+        const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
+        if ((u + 1) * kSub <= seqlen) {
+          // full sub-tile: one uniform base, per-lane 32-bit offsets
 #pragma unroll
-        for (int k = 0; k < kBf16LoadsPerThread; ++k)
-          __builtin_amdgcn_global_load_lds((const void*)(token_ptr(u, dtok[k], page) + dchunk[k] * 16),
-                                           (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024), 16, 0, 0);
+          for (int k = 0; k < kBf16LoadsPerThread; ++k)
+            __builtin_amdgcn_global_load_lds((const void*)(base + doff[k]),
+                                             (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024), 16, 0, 0);
+        } else {
+#pragma unroll
+          for (int k = 0; k < kBf16LoadsPerThread; ++k) {
+            const uint8_t* src = u * kSub + dtok[k] < seqlen ? base + doff[k] : g_zero_token + dchunk[k] * 16;
+            __builtin_amdgcn_global_load_lds((const void*)src,
+                                             (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024), 16, 0, 0);
+          }
+        }
       }
     };
-    auto load_fp8 = [&](int u, int page, RawFp8& r) {
+    auto load_fp8 = [&](int u, RawFp8& r) {
       const int t = tid >> 3, j = tid & 7;
-      const uint8_t* pt = token_ptr(u, t, page);
+      const uint8_t* pt = token_ptr(u, t);
 #pragma unroll
       for (int i = 0; i < 4; ++i) r.v[i] = *(const u32x4*)(pt + 16 * (j + 8 * i));
       r.sc = *(const u32x4*)(pt + kFp8Dims);
@@ -262,145 +367,156 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     float m_ref = kNegInf, m_seen = kNegInf, l_sum = 0.f;
     bool redo = false;
     do {
-    l_sum = 0.f;
+      l_sum = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
+      for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[cb][e] = 0.f;
-    if (redo) m_ref = m_seen + kRefLift;
-    bool overflow = false;
+        for (int e = 0; e < 16; ++e) acc[cb][e] = 0.f;
+      if (redo) m_ref = m_seen + kRefLift;
+      bool overflow = false;
 
-    // ---- prologue: index data for u0 .. u0 + 2, stage u0 (and u0 + 1) --------------
-    int idx_pref = -1;  // sparse: index of slot l32 of sub-tile u + 3 (wave 0)
-    if (SPARSE) {
-      if (wave == 0) {
-        publish(u0, tok_of(idx_at(u0)));
-        publish(u0 + 1, tok_of(idx_at(u0 + 1)));
-        publish(u0 + 2, tok_of(idx_at(u0 + 2)));
-        idx_pref = idx_at(u0 + 3);
-      }
-      __syncthreads();
-    }
-    RawFp8 raw;  // FP8: sub-tile u + 1 in flight in VGPRs
-    if (FP8) {
-      load_fp8(u0, page_of(u0), raw);
-      store_fp8(raw, buffer(u0));
-      if (u0 + 1 < u1) load_fp8(u0 + 1, page_of(u0 + 1), raw);
-    } else {
-      stage_bf16(u0, page_of(u0), buffer(u0));
-      if (u0 + 1 < u1) {
-        stage_bf16(u0 + 1, page_of(u0 + 1), buffer(u0 + 1));
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // sub-tile u0 has landed
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-    }
-    int page_pref = page_of(u0 + 2);  // dense: page of sub-tile u + 2
-    __syncthreads();
-
-    // ---- per sub-tile: part 1 (staging ahead, scores, max) --------------------------
-    float x[16];
-    int tok_pref = -1;
-    auto part1 = [&](int u) -> float {
-      MLA_LDS char* buf = buffer(u);
-      if (SPARSE && wave == 0) {
-        tok_pref = tok_of(idx_pref);  // sub-tile u + 3; its index came last round
-        idx_pref = idx_at(u + 4);
-      }
-      const int page2 = page_pref;
-      page_pref = page_of(u + 3);
-      __builtin_amdgcn_sched_barrier(0);  // index loads stay ahead of the tile loads
-      if (FP8) {
-        if (u + 1 < u1) store_fp8(raw, buffer(u + 1));  // arrived during the last round
-        if (u + 2 < u1) load_fp8(u + 2, page2, raw);
-      } else if (u + 2 < u1) {
-        stage_bf16(u + 2, page2, buffer(u + 2));
-      }
-      // partial S^T over this wave's dims
-      f32x16 s = {};
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
-        const int off = kk < 16 ? kofs[kk & 3] + (kk >> 2) * 128 : kofs_r[kk - 16];
-        const bf16x8 kf = *(MLA_LDS bf16x8*)(buf + off);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
-      }
-      // swap partial scores with the partner wave
-      MLA_LDS f32x4* xo = xbuf + (u & 1) * (4 * 4 * 64) + xo_base;
-      MLA_LDS f32x4* xp = xbuf + (u & 1) * (4 * 4 * 64) + xp_base;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) xo[q4 * 64] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-      lds_barrier();
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 o = xp[q4 * 64];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // both waves add (hf 0 partial) + (hf 1 partial)
-          const float mine = s[4 * q4 + e], theirs = o[e];
-          x[4 * q4 + e] = (hf == 0 ? mine + theirs : theirs + mine) * p.scale_log2;
+      // ---- prologue: metadata, then stage u0 and u0 + 1 ----------------------------
+      int idx_pref = -1;  // FP8 sparse: index of slot l32 of sub-tile u + 4
+      RawFp8 raw;         // FP8: sub-tile u + 1 in flight in VGPRs
+      if constexpr (FP8) {
+        int v0, v1, v2;
+        if (SPARSE) {
+          v0 = tok_of(idx_at(u0));
+          v1 = tok_of(idx_at(u0 + 1));
+          v2 = tok_of(idx_at(u0 + 2));
+          idx_pref = idx_at(u0 + 3);
+        } else {
+          v0 = page_load(u0);
+          v1 = page_load(u0 + 1);
+          v2 = page_load(u0 + 2);
         }
+        if (wave == 0) {
+          publish(u0, v0);
+          publish(u0 + 1, v1);
+          publish(u0 + 2, v2);
+        }
+        __syncthreads();
+        load_fp8(u0, raw);
+        store_fp8(raw, buffer(u0));
+        load_fp8(u0 + 1, raw);
+        __syncthreads();
+      } else {
+        meta_fill();
+        __syncthreads();
+        stage_bf16(u0, buffer(u0));
+        stage_bf16(u0 + 1, buffer(u0 + 1));
+        tile_barrier_keep<kBf16LoadsPerThread>();  // sub-tile u0 has landed
       }
-      // mask: lane holds row l32, tokens 8 (e / 4) + 4 h + e % 4
-      const bool full = SPARSE ? vmask[u & 3] == 0xFFFFFFFFu : (u + 1) * kSub <= seqlen;
-      if (!full) {
-        const uint32_t tmask = SPARSE ? vmask[u & 3] : 0u;
-        const int vcount = seqlen - u * kSub;
+
+      float x[16];
+      // One round: compute sub-tile u from buf while filling nxt (FP8: sub-tile
+      // u + 1 from registers; BF16: sub-tile u + 2 by direct loads).  The two
+      // buffers are distinct, and saying so (restrict) lets the compiler keep the
+      // direct loads in flight across the reads of buf.
+      auto round = [&](const int u, MLA_LDS char* __restrict__ buf,
+                       MLA_LDS char* __restrict__ nxt) __attribute__((always_inline)) {
+        int meta = 0;  // FP8: metadata of sub-tile u + 3 (published at the end of this round)
+        if constexpr (FP8) {
+          if (SPARSE) {
+            meta = tok_of(idx_pref);
+            idx_pref = idx_at(u + 4);
+          } else {
+            meta = page_load(u + 3);
+          }
+        } else {
+          meta_dma(u);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // metadata loads stay ahead of the tile loads
+        // stream sub-tile u + 2 (its buffer was freed by the barrier ending round u - 1)
+        if (FP8) {
+          store_fp8(raw, nxt);  // sub-tile u + 1 arrived during the last round
+          load_fp8(u + 2, raw);
+        } else {
+          stage_bf16(u + 2, nxt);
+        }
+        // partial S^T over this wave's dims
+        f32x16 s = {};
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) {
+          const int off = kk < 16 ? kofs[kk & 3] + (kk >> 2) * 128 : kofs_r[kk - 16];
+          const bf16x8 kf = *(MLA_LDS bf16x8*)(buf + off);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
+        }
+        // swap partial scores with the partner wave
+        MLA_LDS f32x4* xo = xbuf + (u & 1) * (4 * 4 * 64) + xo_base;
+        MLA_LDS f32x4* xp = xbuf + (u & 1) * (4 * 4 * 64) + xp_base;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) xo[q4 * 64] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+        lds_barrier();
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 o = xp[q4 * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // both waves add (hf 0 partial) + (hf 1 partial)
+            const float mine = s[4 * q4 + e], theirs = o[e];
+            x[4 * q4 + e] = (hf == 0 ? mine + theirs : theirs + mine) * p.scale_log2;
+          }
+        }
+        // mask: lane holds row l32, tokens 8 (e / 4) + 4 h + e % 4
+        const uint32_t tmask = SPARSE ? sparse_mask(u) : 0u;
+        const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= seqlen;
+        if (!full) {
+          const int vcount = seqlen - u * kSub;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int tok = 8 * (e >> 2) + 4 * h + (e & 3);
+            const bool ok = SPARSE ? ((tmask >> tok) & 1u) != 0 : tok < vcount;
+            x[e] = ok ? x[e] : kNegInf;
+          }
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        m_seen = fmaxf(m_seen, mx);
+        if (m_ref == kNegInf && mx != kNegInf) m_ref = mx + kRefLift;
+        overflow |= mx > m_ref + kRefRoom;
+
+        // probabilities and O^T += V^T P^T over two 16-token k-steps
+        const float msafe = m_ref == kNegInf ? 0.f : m_ref;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int tok = 8 * (e >> 2) + 4 * h + (e & 3);
-          const bool ok = SPARSE ? ((tmask >> tok) & 1u) != 0 : tok < vcount;
-          x[e] = ok ? x[e] : kNegInf;
+          x[e] = __builtin_amdgcn_exp2f(x[e] - msafe);
+          l_sum += x[e];
         }
-      }
-      float mx = x[0];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
-      return fmaxf(mx, __shfl_xor(mx, 32));
-    };
-    // ---- part 2 (probabilities, O^T += V^T P^T, hand over to the next sub-tile) ----
-    auto part2 = [&](int u) {
-      MLA_LDS char* buf = buffer(u);
-      const float msafe = m_ref == kNegInf ? 0.f : m_ref;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          bf16x8 pb;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        x[e] = __builtin_amdgcn_exp2f(x[e] - msafe);
-        l_sum += x[e];
-      }
+          for (int e = 0; e < 8; ++e) pb[e] = (__bf16)x[8 * s2 + e];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)x[8 * s2 + e];
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][0][cb & 1] + 64 * cb));
-          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][1][cb & 1] + 64 * cb));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[cb], 0, 0, 0);
+          for (int cb = 0; cb < 8; ++cb) {
+            const i16x4 a0 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][0][cb & 1] + 64 * cb));
+            const i16x4 a1 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][1][cb & 1] + 64 * cb));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[cb], 0, 0, 0);
+          }
         }
-      }
-      if (SPARSE && wave == 0) publish(u + 3, tok_pref);
-      if (FP8)
-        lds_barrier();  // sub-tile u + 1 went through registers; u + 2 stays in flight
-      else if (u + 2 < u1)
-        tile_barrier_keep9();  // u + 1 landed, u + 2 may still fly
-      else
-        tile_barrier_drain();
-    };
+        if constexpr (FP8) {
+          if (wave == 0) publish(u + 3, meta);
+          lds_barrier();  // sub-tile u + 1 went through registers; u + 2 stays in flight
+        } else {
+          // this round's direct loads may still fly; everything before has landed
+          tile_barrier_keep<kBf16LoadsPerThread + (SPARSE ? 2 : 1)>();
+        }
+      };
+      for (int u = u0; u < u1; ++u) round(u, buffer(u), buffer(u + (FP8 ? 1 : 2)));
+      // tiles staged past the end are still in flight: let them land before LDS is reused
+      tile_barrier_drain();
 
-    // ---- main loop ---------------------------------------------------------------------
-    for (int u = u0; u < u1; ++u) {
-      const float mx = part1(u);
-      m_seen = fmaxf(m_seen, mx);
-      if (m_ref == kNegInf && mx != kNegInf) m_ref = mx + kRefLift;
-      overflow |= mx > m_ref + kRefRoom;
-      part2(u);
-    }
-    // the restart must be taken by the whole workgroup (it contains barriers)
-    if (lane == 0) wflag[wave] = __ballot(overflow) != 0 ? 1 : 0;
-    __syncthreads();
-    redo = (wflag[0] | wflag[1] | wflag[2] | wflag[3]) != 0;
-    __syncthreads();
+      // the restart must be taken by the whole workgroup (it contains barriers)
+      if (lane == 0) wflag[wave] = __ballot(overflow) != 0 ? 1 : 0;
+      __syncthreads();
+      redo = (wflag[0] | wflag[1] | wflag[2] | wflag[3]) != 0;
+      __syncthreads();
     } while (redo);
 
     // ---- epilogue -------------------------------------------------------------------
