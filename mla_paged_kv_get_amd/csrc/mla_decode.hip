@@ -434,14 +434,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
         } else {
           stage_bf16(u + 2, nxt);
         }
-        // partial S^T over this wave's dims
-        f32x16 s = {};
+        // partial S^T over this wave's dims; the K fragments are read six ahead of
+        // the MFMA that consumes them, so LDS latency hides behind the MFMA chain
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 kf[18];
 #pragma unroll
         for (int kk = 0; kk < 18; ++kk) {
           const int off = kk < 16 ? kofs[kk & 3] + (kk >> 2) * 128 : kofs_r[kk - 16];
-          const bf16x8 kf = *(MLA_LDS bf16x8*)(buf + off);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
+          kf[kk] = *(MLA_LDS bf16x8*)(buf + off);
         }
+        f32x16 s = {};
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int kk = 0; kk < 12; ++kk) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         // swap partial scores with the partner wave
         MLA_LDS f32x4* xo = xbuf + (u & 1) * (4 * 4 * 64) + xo_base;
         MLA_LDS f32x4* xp = xbuf + (u & 1) * (4 * 4 * 64) + xp_base;
@@ -458,6 +469,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
             x[4 * q4 + e] = (hf == 0 ? mine + theirs : theirs + mine) * p.scale_log2;
           }
         }
+        // V^T fragments of the first 16 tokens: they do not depend on P, so they
+        // are read while the softmax runs
+        auto vread = [&](int s2, int cb) -> bf16x8 {
+          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][0][cb & 1] + 64 * cb));
+          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][1][cb & 1] + 64 * cb));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 va0[8];
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) va0[cb] = vread(0, cb);
         // mask: lane holds row l32, tokens 8 (e / 4) + 4 h + e % 4
         const uint32_t tmask = SPARSE ? sparse_mask(u) : 0u;
         const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= seqlen;
@@ -485,21 +506,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
           x[e] = __builtin_amdgcn_exp2f(x[e] - msafe);
           l_sum += x[e];
         }
+        bf16x8 pb0, pb1;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          bf16x8 pb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[e] = (__bf16)x[8 * s2 + e];
-#pragma unroll
-          for (int cb = 0; cb < 8; ++cb) {
-            const i16x4 a0 =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][0][cb & 1] + 64 * cb));
-            const i16x4 a1 =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][1][cb & 1] + 64 * cb));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[cb], 0, 0, 0);
-          }
+        for (int e = 0; e < 8; ++e) {
+          pb0[e] = (__bf16)x[e];
+          pb1[e] = (__bf16)x[8 + e];
         }
+        // second 16 tokens' V^T reads interleaved with the first 16 tokens' MFMAs
+        bf16x8 va1[8];
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+          va1[cb] = vread(1, cb);
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0[cb], pb0, acc[cb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1[cb], pb1, acc[cb], 0, 0, 0);
         if constexpr (FP8) {
           if (wave == 0) publish(u + 3, meta);
           lds_barrier();  // sub-tile u + 1 went through registers; u + 2 stays in flight
