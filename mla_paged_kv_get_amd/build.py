@@ -76,6 +76,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link failed")
+    # every symbol must resolve (a kernel the host pass failed to emit shows up here)
+    import ctypes
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    except OSError as e:
+        os.unlink(tmp)
+        raise RuntimeError("linked library does not load: %s" % e)
     os.replace(tmp, LIB)
     if verbose:
         print(report)

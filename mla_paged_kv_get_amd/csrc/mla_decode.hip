@@ -61,6 +61,16 @@ __device__ __forceinline__ void tile_barrier_drain() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Direct buffer loads into LDS: lane i writes 16 (or 4) bytes at dst + 16 i (4 i);
+// an offset past the resource's size loads zeros.  (Kept out of lambdas: there
+// the builtin makes the host pass drop the kernel.)
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, MLA_LDS void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t rs, MLA_LDS void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
+}
+
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRefLift = 32.0f;   // log2 units
 constexpr float kRefRoom = 88.0f;
@@ -77,6 +87,8 @@ constexpr int kMetaBytes = 2 * kRing * 64 * 4;
 constexpr int kFlagOffset = kMetaOffset + kMetaBytes;  // int32 per-wave flags[4]
 constexpr int kLdsBytes = kFlagOffset + 4 * 4;
 constexpr int kBf16LoadsPerThread = kSubBytes / 16 / kThreads;  // 9
+// Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle.
+constexpr int kBufferFlags = 0x00020000;
 
 // FP8 registers of one sub-tile for this thread: token tid / 8, code chunks
 // j + 8 i (i = 0..3, j = tid % 8; chunk i uses scale i), the four scales and
@@ -183,6 +195,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     const int seqlen = p.seqlens[b];
     const int32_t* bt_row = p.block_table + (int64_t)b * p.max_blocks;
     const int32_t* idx_row = SPARSE ? p.indices + (int64_t)stream * p.topk : nullptr;
+    const __amdgpu_buffer_rsrc_t bt_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)bt_row, 0, p.max_blocks * 4, kBufferFlags);
     // sub-tiles [u0, u1): 32 tokens (dense) or 32 index slots (sparse) each
     const int limit = SPARSE ? p.topk : seqlen;
     const int u0 = 2 * lo;
@@ -239,8 +253,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
                                          (MLA_LDS void*)(ring_pg + ((u + 4) & (kRing - 1)) * 64), 4, 0, 0);
       } else {
         // page of sub-tile u + 4 (the split's last page past its end)
-        __builtin_amdgcn_global_load_lds((const void*)(bt_row + (min(u + 4, u1 - 1) >> 1)),
-                                         (MLA_LDS void*)(ring_pg + ((u + 4) & (kRing - 1)) * 64), 4, 0, 0);
+        buffer_load_lds4(bt_rs, (MLA_LDS void*)(ring_pg + ((u + 4) & (kRing - 1)) * 64),
+                         (uint32_t)(min(u + 4, u1 - 1) >> 1) * 4u);
       }
     };
     // BF16 prologue: the same ring entries by plain loads (rings for u0 .. u0 + 5)
@@ -303,7 +317,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       const int page = tokidx[(u & 3) * kSub];
       return p.kv + ((int64_t)page * kPage + (u & 1) * kSub + t) * tok_bytes;
     };
-    auto stage_bf16 = [&](int u, MLA_LDS char* buf) {
+    // BF16 direct loads of sub-tile u: this thread's nine 16-byte pieces.  Dense
+    // tiles use buffer loads against the sub-tile's 36,864 bytes, and tokens past
+    // the sequence end take an out-of-range offset, which loads zeros; sparse
+    // tiles load from per-lane global addresses (the zero token when a slot is
+    // not attended).
+    struct Bf16Loads {
+      __amdgpu_buffer_rsrc_t rs;
+      uint32_t voff[kBf16LoadsPerThread];
+      const uint8_t* src[kBf16LoadsPerThread];
+    };
+    auto stage_prep = [&](int u, Bf16Loads& L) {
       const int r = (u & (kRing - 1)) * 64;
       if constexpr (SPARSE) {
         // token row of slot l32, then of each load's token
@@ -313,28 +337,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
 #pragma unroll
         for (int k = 0; k < kBf16LoadsPerThread; ++k) {
           const int tk = __shfl(tok, dtok[k]);
-          const uint8_t* src = tk >= 0 ? p.kv + (int64_t)tk * kBf16TokenBytes : g_zero_token;
-          __builtin_amdgcn_global_load_lds((const void*)(src + dchunk[k] * 16),
-                                           (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024), 16, 0, 0);
+          L.src[k] = (tk >= 0 ? p.kv + (int64_t)tk * kBf16TokenBytes : g_zero_token) + dchunk[k] * 16;
         }
       } else {
         const int page = __builtin_amdgcn_readfirstlane(ring_pg[r]);
         const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
-        if ((u + 1) * kSub <= seqlen) {
-          // full sub-tile: one uniform base, per-lane 32-bit offsets
+        L.rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, kSubBytes, kBufferFlags);
+        const int valid = seqlen - u * kSub;  // tokens of the sub-tile inside the sequence
 #pragma unroll
-          for (int k = 0; k < kBf16LoadsPerThread; ++k)
-            __builtin_amdgcn_global_load_lds((const void*)(base + doff[k]),
-                                             (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024), 16, 0, 0);
-        } else {
-#pragma unroll
-          for (int k = 0; k < kBf16LoadsPerThread; ++k) {
-            const uint8_t* src = u * kSub + dtok[k] < seqlen ? base + doff[k] : g_zero_token + dchunk[k] * 16;
-            __builtin_amdgcn_global_load_lds((const void*)src,
-                                             (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024), 16, 0, 0);
-          }
-        }
+        for (int k = 0; k < kBf16LoadsPerThread; ++k) L.voff[k] = dtok[k] < valid ? doff[k] : (uint32_t)kSubBytes;
       }
+    };
+    auto stage_issue = [&](const Bf16Loads& L, int k, MLA_LDS char* buf) {
+      MLA_LDS void* dst = (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024);
+      if constexpr (SPARSE)
+        __builtin_amdgcn_global_load_lds((const void*)L.src[k], dst, 16, 0, 0);
+      else
+        buffer_load_lds16(L.rs, dst, L.voff[k]);
+    };
+    auto stage_bf16 = [&](int u, MLA_LDS char* buf) {
+      Bf16Loads L;
+      stage_prep(u, L);
+#pragma unroll
+      for (int k = 0; k < kBf16LoadsPerThread; ++k) stage_issue(L, k, buf);
     };
     auto load_fp8 = [&](int u, RawFp8& r) {
       const int t = tid >> 3, j = tid & 7;
@@ -427,50 +452,49 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
           meta_dma(u);
         }
         __builtin_amdgcn_sched_barrier(0);  // metadata loads stay ahead of the tile loads
-        // stream sub-tile u + 2 (its buffer was freed by the barrier ending round u - 1)
-        if (FP8) {
+        // stream sub-tile u + 2 (its buffer was freed by the barrier ending round u - 1):
+        // FP8 converts the registers loaded last round and loads the next; BF16
+        // prepares its nine direct loads here and issues them between the QK MFMAs
+        Bf16Loads L;
+        if constexpr (FP8) {
           store_fp8(raw, nxt);  // sub-tile u + 1 arrived during the last round
           load_fp8(u + 2, raw);
         } else {
-          stage_bf16(u + 2, nxt);
+          stage_prep(u + 2, L);
         }
-        // partial S^T over this wave's dims; the K fragments are read six ahead of
-        // the MFMA that consumes them, so LDS latency hides behind the MFMA chain
-        __builtin_amdgcn_sched_barrier(0);
+        // partial S^T over this wave's dims.  Issue order is pinned (a scheduling
+        // barrier per step): the K fragments are read six MFMAs ahead, so the LDS
+        // reads overlap the MFMA chain.
+        constexpr int kAhead = 6;
         bf16x8 kf[18];
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
+        auto kread = [&](int kk) {
           const int off = kk < 16 ? kofs[kk & 3] + (kk >> 2) * 128 : kofs_r[kk - 16];
           kf[kk] = *(MLA_LDS bf16x8*)(buf + off);
-        }
+        };
+#pragma unroll
+        for (int kk = 0; kk < kAhead; ++kk) kread(kk);
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s = {};
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int kk = 0; kk < 12; ++kk) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int kk = 0; kk < 18; ++kk) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+          if (kk + kAhead < 18) kread(kk + kAhead);
+          if constexpr (!FP8) {
+            if (kk < kBf16LoadsPerThread) stage_issue(L, kk, nxt);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         // swap partial scores with the partner wave
         MLA_LDS f32x4* xo = xbuf + (u & 1) * (4 * 4 * 64) + xo_base;
         MLA_LDS f32x4* xp = xbuf + (u & 1) * (4 * 4 * 64) + xp_base;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) xo[q4 * 64] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
         lds_barrier();
+        f32x4 xr[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 o = xp[q4 * 64];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // both waves add (hf 0 partial) + (hf 1 partial)
-            const float mine = s[4 * q4 + e], theirs = o[e];
-            x[4 * q4 + e] = (hf == 0 ? mine + theirs : theirs + mine) * p.scale_log2;
-          }
-        }
-        // V^T fragments of the first 16 tokens: they do not depend on P, so they
-        // are read while the softmax runs
+        for (int q4 = 0; q4 < 4; ++q4) xr[q4] = xp[q4 * 64];
+        // V^T fragments of the first 16 tokens do not depend on P: they are read
+        // while the softmax runs
         auto vread = [&](int s2, int cb) -> bf16x8 {
           const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][0][cb & 1] + 64 * cb));
           const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][1][cb & 1] + 64 * cb));
@@ -479,6 +503,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
         bf16x8 va0[8];
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) va0[cb] = vread(0, cb);
+        __builtin_amdgcn_sched_barrier(0);
+        // raw scores S = (hf 0 partial) + (hf 1 partial), the same sum in both waves
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float mine = s[4 * q4 + e], theirs = xr[q4][e];
+            x[4 * q4 + e] = hf == 0 ? mine + theirs : theirs + mine;
+          }
         // mask: lane holds row l32, tokens 8 (e / 4) + 4 h + e % 4
         const uint32_t tmask = SPARSE ? sparse_mask(u) : 0u;
         const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= seqlen;
@@ -491,19 +524,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
             x[e] = ok ? x[e] : kNegInf;
           }
         }
+        // row maximum in the log2 domain (the scale is positive)
         float mx = x[0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
         m_seen = fmaxf(m_seen, mx);
         if (m_ref == kNegInf && mx != kNegInf) m_ref = mx + kRefLift;
         overflow |= mx > m_ref + kRefRoom;
 
-        // probabilities and O^T += V^T P^T over two 16-token k-steps
+        // P = 2^(scale_log2 S - m_ref) and O^T += V^T P^T over two 16-token k-steps
         const float msafe = m_ref == kNegInf ? 0.f : m_ref;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          x[e] = __builtin_amdgcn_exp2f(x[e] - msafe);
+          x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], p.scale_log2, -msafe));
           l_sum += x[e];
         }
         bf16x8 pb0, pb1;
@@ -512,12 +546,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
           pb0[e] = (__bf16)x[e];
           pb1[e] = (__bf16)x[8 + e];
         }
+        __builtin_amdgcn_sched_barrier(0);
         // second 16 tokens' V^T reads interleaved with the first 16 tokens' MFMAs
         bf16x8 va1[8];
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
-          va1[cb] = vread(1, cb);
           acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0[cb], pb0, acc[cb], 0, 0, 0);
+          va1[cb] = vread(1, cb);
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1[cb], pb1, acc[cb], 0, 0, 0);
