@@ -10,8 +10,8 @@
 //   N = total tiles, q = max(ceil(N / W), min_tiles, 1);
 //   worker w owns global tiles [w q, min((w + 1) q, N)) of the streams laid end
 //   to end; each stream's splits are the workers that meet it, in worker order.
-// One workgroup of 256 threads: chunked prefix sums over the streams, then one
-// binary search per worker.  Up to kLdsStreams streams the prefix arrays live in
+// One workgroup of 256 threads: chunked prefix sums (a shuffle scan across the
+// threads' chunk sums) over the streams, then one binary search per worker.  Up to kLdsStreams streams the prefix arrays live in
 // LDS (the searches then cost no global round trips); beyond that they are
 // built in place in the metadata buffer.
 #include "mla_common.hpp"
@@ -28,15 +28,29 @@ __device__ __forceinline__ int64_t stream_tiles(const int32_t* seqlens, int topk
   return len > 0 ? (len + kPage - 1) / kPage : 0;
 }
 
-// Exclusive scan of part[0..256) in place by one thread; returns the total.
-__device__ int64_t scan_parts(int64_t* part) {
-  int64_t acc = 0;
-  for (int k = 0; k < kSchedThreads; ++k) {
-    const int64_t t = part[k];
-    part[k] = acc;
-    acc += t;
+// Exclusive scan of one value per thread over the workgroup; every thread gets
+// its exclusive prefix and the total.  Wave-level shuffles, then the four wave
+// totals through LDS.
+__device__ int64_t block_exclusive_scan(int64_t v, int64_t* wave_sums, int64_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
   }
-  return acc;
+  if (lane == 63) wave_sums[wave] = inc;
+  __syncthreads();
+  int64_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kSchedThreads / 64; ++w) {
+    const int64_t ws = wave_sums[w];
+    if (w < wave) before += ws;
+    total += ws;
+  }
+  __syncthreads();  // wave_sums is reused by the next scan
+  return before + inc - v;
 }
 
 // First index in [0, n) with a[idx] > x (n if none); a non-decreasing.
@@ -55,8 +69,7 @@ __device__ int upper_bound(const int32_t* a, int n, int64_t x) {
 __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t* __restrict__ seqlens, int B, int s_q,
                                                                   int h_q, int topk, int W, int min_tiles,
                                                                   int32_t* __restrict__ meta) {
-  __shared__ int64_t part[kSchedThreads];
-  __shared__ int64_t total_tiles, quantum, total_splits;
+  __shared__ int64_t wave_sums[kSchedThreads / 64];
   __shared__ int32_t lds_first[kLdsStreams + 1], lds_split[kLdsStreams + 1];
   const int tid = threadIdx.x;
   const int n = topk > 0 ? B * s_q : B;
@@ -73,27 +86,16 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t*
   // tile prefix sums
   int64_t sum = 0;
   for (int i = lo; i < hi; ++i) sum += stream_tiles(seqlens, topk, i);
-  part[tid] = sum;
-  __syncthreads();
-  if (tid == 0) {
-    const int64_t N = scan_parts(part);
-    int64_t q = (N + W - 1) / W;
-    if (q < min_tiles) q = min_tiles;
-    if (q < 1) q = 1;
-    total_tiles = N;
-    quantum = q;
-    first[n] = (int32_t)N;
+  int64_t N;
+  int64_t acc = block_exclusive_scan(sum, wave_sums, N);
+  for (int i = lo; i < hi; ++i) {
+    first[i] = (int32_t)acc;
+    acc += stream_tiles(seqlens, topk, i);
   }
-  __syncthreads();
-  {
-    int64_t acc = part[tid];
-    for (int i = lo; i < hi; ++i) {
-      first[i] = (int32_t)acc;
-      acc += stream_tiles(seqlens, topk, i);
-    }
-  }
-  const int64_t N = total_tiles, q = quantum;
-  __syncthreads();
+  if (tid == 0) first[n] = (int32_t)N;
+  int64_t q = (N + W - 1) / W;
+  if (q < min_tiles) q = min_tiles;
+  if (q < 1) q = 1;
 
   // splits per stream = workers meeting it
   sum = 0;
@@ -101,21 +103,14 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t*
     const int64_t t = stream_tiles(seqlens, topk, i);
     sum += t == 0 ? 0 : ((int64_t)first[i] + t - 1) / q - (int64_t)first[i] / q + 1;
   }
-  part[tid] = sum;
-  __syncthreads();
-  if (tid == 0) {
-    total_splits = scan_parts(part);
-    split_off[n] = (int32_t)total_splits;
+  int64_t total_splits;
+  acc = block_exclusive_scan(sum, wave_sums, total_splits);
+  for (int i = lo; i < hi; ++i) {
+    split_off[i] = (int32_t)acc;
+    const int64_t t = stream_tiles(seqlens, topk, i);
+    acc += t == 0 ? 0 : ((int64_t)first[i] + t - 1) / q - (int64_t)first[i] / q + 1;
   }
-  __syncthreads();
-  {
-    int64_t acc = part[tid];
-    for (int i = lo; i < hi; ++i) {
-      split_off[i] = (int32_t)acc;
-      const int64_t t = stream_tiles(seqlens, topk, i);
-      acc += t == 0 ? 0 : ((int64_t)first[i] + t - 1) / q - (int64_t)first[i] / q + 1;
-    }
-  }
+  if (tid == 0) split_off[n] = (int32_t)total_splits;
   __syncthreads();
 
   // per-worker ranges

@@ -76,6 +76,25 @@ def test_metadata_matches_schedule_rule(seed):
     assert m[5] == off_ref[-1]
 
 
+@pytest.mark.parametrize("B,s_q,topk,W", [(3000, 1, 0, 256), (700, 2, 2048, 512), (12000, 1, 64, 1024),
+                                        (257, 1, 0, 3)])
+def test_metadata_many_streams(B, s_q, topk, W):
+    """Streams spread over several per-thread chunks, and (above 8192 streams) the
+    prefix arrays built in global memory instead of LDS."""
+    import mla_paged_kv_get_amd as mla
+
+    rng = np.random.default_rng(B + W)
+    seqlens = rng.integers(0, 5000, size=B).astype(np.int32)
+    seqlens[rng.random(B) < 0.1] = 0
+    say("[gpu] metadata many streams B=%d s_q=%d topk=%d W=%d" % (B, s_q, topk, W))
+    meta = mla.mla_get_metadata(torch.from_numpy(seqlens).to(DEV), s_q, 64, 1, topk, False, W)
+    m = meta.tensor.cpu().numpy()
+    n_streams = B * s_q if topk else B
+    sched_ref, off_ref = oracle.schedule(seqlens, s_q, topk, W, int(m[7]))
+    assert np.array_equal(m[16:16 + 8 * W].reshape(W, 8), sched_ref)
+    assert np.array_equal(m[16 + 8 * W:16 + 8 * W + n_streams + 1], off_ref)
+
+
 # --------------------------------------------------------------------------------------
 # small parity cases: several tiles, ragged tails, every variant
 
@@ -182,6 +201,19 @@ def test_deterministic():
     o1, l1, m = run_gpu(prob, dev_inputs=d)
     o2, l2, _ = run_gpu(prob, dev_inputs=d, meta=m)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_metadata_reused_across_calls():
+    """The split merge counts arrivals in the metadata; every call must leave the
+    counters as it found them, so one metadata serves many calls (one per layer)."""
+    prob = mi.make_problem("reuse", 5, 1, 128, [0, 2000, 700, 64, 1500], seed=85, max_blocks=32)
+    d = to_device(prob)
+    o_ref, lse_ref = oracle.problem_decode(prob)
+    m = None
+    for call in range(3):
+        o, l, m = run_gpu(prob, 1000, dev_inputs=d, meta=m)
+        o, l = flat(o, l)
+        compare(o, l, o_ref, lse_ref, "call %d with shared metadata" % call)
 
 
 def test_lse_merge_through_the_abi():
