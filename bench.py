@@ -1,24 +1,40 @@
 """Benchmark of MLA decode over a paged latent KV cache on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs 2,3,4,5]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 2,3,4,5]
+                [--no-cpu-baseline] [--calibrate-copy]
 
-A step is one pass of the decode path over one batch: the scheduler kernel
-(mla_get_metadata) and the decode call (split-KV decode + lse combine).  The
-headline workload is the memory-bound dense BF16 decode (B=64, h_q=128,
-seqlen 4096, block 64, shuffled pages); the other workloads (dense s_q=2
-compute-bound, sparse FP8 top-2048, skewed long-context sparse FP8) are
-measured the same way and reported under "workloads".  All inputs are seeded
-synthetic data resident in HBM before timing.
+A step is one pass of the whole decode path over one batch of synthetic input
+already resident in HBM: the scheduler kernel (mla_get_metadata) and the decode
+call (mla_decode_with_kvcache: the split-KV decode kernel, then the lse combine
+kernel).  The headline workload is the memory-bound dense BF16 decode (B=64,
+s_q=1, h_q=128, seqlen 4096 for all, block 64, pages a random permutation of
+the pool); it is the one the JSON line reports.  --workloads adds the other
+configurations (dense s_q=2 compute-bound, sparse FP8 top-2048, skewed sparse
+FP8) under "workloads", measured the same way.
 
-Counting: FLOPs = 2 (576 + 512) per query row per attended token; bytes = KV
-bytes of the attended tokens (1152 B per bf16 token, 656 B per FP8 token) +
-q + o.  Peaks: 8.0 TB/s HBM, 2.5 PFLOP/s dense bf16 MFMA.
+Counting (per decode call): FLOPs = 2 (576 + 512) per query row per attended
+token; algorithmic bytes = KV bytes of the attended tokens (1152 B per bf16
+token, 656 B per FP8 token) + q + o.  Peaks: 8.0 TB/s HBM, 2.5 PFLOP/s dense
+bf16 MFMA.
+
+roofline: the dominant kernel is the split-KV decode kernel; its duration is
+taken per launch over the timed steps with HIP events recorded on its stream
+right around it (mla_set_decode_kernel_events).  Every timed region starts
+behind a short GPU spin (torch.cuda._sleep), so the host has queued the work
+before the GPU reaches it and the events measure GPU time, not launch overhead.  "traffic" is the HBM bytes per
+launch that rocprofv3 FETCH_SIZE + WRITE_SIZE measured for that kernel on this
+workload (scaled by the same counters' reading of a plain copy of known size),
+read from profiles/; it is null when the kernel sources changed since.
+
+--calibrate-copy runs only a plain 1 GiB device-to-device copy (8 times), the
+known-size reference the traffic counters are scaled by.
 
 Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,20 +47,60 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 METRIC = "decode TFLOP/s + HBM GB/s vs MI355X roofline; dense bf16 & sparse fp8 MLA"
 HEADLINE = 2
+KERNEL_SOURCES = ["mla_paged_kv_get_amd/csrc/mla_decode.hip", "mla_paged_kv_get_amd/csrc/mla_device.hpp",
+                  "mla_paged_kv_get_amd/csrc/mla_common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mla_decode_kernel_dense_bf16_b64_h128_s4096.json")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--configs", default="2,3,4,5")
+    ap.add_argument("--workloads", default="2", help="comma list of configurations; 2 (the headline) is always run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold", action="store_true", help="also time each step after overwriting 1 GiB (cold caches)")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--no-headline", action="store_true",
+                    help="run only the --workloads listed (the first one is reported); for per-workload profiles")
     return ap.parse_args()
 
 
-def measure(cfg: int, steps: int, warmup: int, cold: bool):
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode kernel on the headline workload, if the
+    committed counter summary was taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(8):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 8}))
+
+
+def measure(cfg: int, steps: int, warmup: int):
     import torch
 
     import mla_inputs as mi
@@ -64,113 +120,145 @@ def measure(cfg: int, steps: int, warmup: int, cold: bool):
     ws = torch.empty(meta.workspace_bytes, dtype=torch.uint8, device=dev)
     o = torch.empty((prob.B, prob.s_q, prob.h_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((prob.B, prob.s_q, prob.h_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
 
-    def step():
-        m = mla.mla_get_metadata(sl, prob.s_q, prob.h_q, 1, topk, prob.is_fp8)
+    def decode_call(m):
         mla.mla_decode_with_kvcache(q, kv, bt, sl, 512, m, idx, prob.is_fp8, prob.softmax_scale, ws, o, lse)
 
-    def decode_only():
-        mla.mla_decode_with_kvcache(q, kv, bt, sl, 512, meta, idx, prob.is_fp8, prob.softmax_scale, ws, o, lse)
+    def step():
+        decode_call(mla.mla_get_metadata(sl, prob.s_q, prob.h_q, 1, topk, prob.is_fp8, out=meta.tensor))
+
+    def hold_gpu(us: float):
+        # keep the GPU busy while the host queues the timed work behind it, so
+        # events time the GPU and not the host's launch overhead
+        torch.cuda._sleep(int(us * 2500))
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+
+    # timed steps (scheduler + decode call); the decode kernel of each step is
+    # bracketed by its own pair of HIP events on its stream
+    timer = mla.DecodeKernelTimer()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    hold_gpu(400.0 * steps + 2000.0)
     e0.record(stream)
     for _ in range(steps):
-        step()
+        timer.record(step)
     e1.record(stream)
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / steps
+    kern = sorted(timer.durations_ms())
+    kernel_ms = sum(kern) / len(kern)
 
-    # decode call alone (metadata reused, as across layers), per-launch events
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in evs:
-        a.record(stream)
-        decode_only()
-        b.record(stream)
-    torch.cuda.synchronize()
-    dec = sorted(a.elapsed_time(b) for a, b in evs)
-    dec_ms = sum(dec) / len(dec)
-    res = dict(config=cfg, name=prob.name, gen_s=round(gen_s, 2), flops=prob.flops(), bytes=prob.bytes(),
-               num_workers=meta.num_workers, step_ms=step_ms, decode_ms=dec_ms, decode_ms_median=dec[len(dec) // 2])
-    if cold:
-        junk = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # decode call alone (metadata reused, as across layers): warm, then cold
+    # (1 GiB written between calls, so the KV pool is not served from the MALL)
+    def timed_calls(cold: bool):
+        junk = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if cold else None
         times = []
         for _ in range(steps):
-            junk.fill_(1)
+            if cold:
+                junk.fill_(1)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            hold_gpu(500.0)
             a.record(stream)
-            decode_only()
+            decode_call(meta)
             b.record(stream)
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b))
         times.sort()
-        res["decode_ms_cold_median"] = times[len(times) // 2]
-        del junk
-    res["tflops"] = prob.flops() / (dec_ms * 1e-3) / 1e12
-    res["gbps"] = prob.bytes() / (dec_ms * 1e-3) / 1e9
-    res["frac_hbm"] = res["gbps"] / PEAK_HBM_GBS
-    res["frac_mfma"] = res["tflops"] / PEAK_BF16_TFLOPS
+        return times[len(times) // 2]
+
+    call_warm = timed_calls(False)
+    call_cold = timed_calls(True)
+    # the scheduler kernel alone
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_gpu(100.0 * steps + 2000.0)
+    a.record(stream)
+    for _ in range(steps):
+        mla.mla_get_metadata(sl, prob.s_q, prob.h_q, 1, topk, prob.is_fp8, out=meta.tensor)
+    b.record(stream)
+    torch.cuda.synchronize()
+    sched_ms = a.elapsed_time(b) / steps
+
+    flops, nbytes = prob.flops(), prob.bytes()
+    res = dict(config=cfg, name=prob.name, gen_s=round(gen_s, 2), flops=flops, bytes=nbytes,
+               num_workers=meta.num_workers, splits=meta.total_splits(),
+               step_us=round(step_ms * 1e3, 2), decode_kernel_us=round(kernel_ms * 1e3, 2),
+               decode_kernel_us_median=round(kern[len(kern) // 2] * 1e3, 2),
+               decode_call_us_warm_median=round(call_warm * 1e3, 2),
+               decode_call_us_cold_median=round(call_cold * 1e3, 2), scheduler_us=round(sched_ms * 1e3, 2),
+               step_tflops=round(flops / (step_ms * 1e-3) / 1e12, 2),
+               kernel_tflops=round(flops / (kernel_ms * 1e-3) / 1e12, 2),
+               kernel_gbps=round(nbytes / (kernel_ms * 1e-3) / 1e9, 1),
+               call_cold_tflops=round(flops / (call_cold * 1e-3) / 1e12, 2),
+               call_cold_gbps=round(nbytes / (call_cold * 1e-3) / 1e9, 1))
+    res["kernel_frac_hbm"] = round(res["kernel_gbps"] / PEAK_HBM_GBS, 4)
+    res["kernel_frac_mfma"] = round(res["kernel_tflops"] / PEAK_BF16_TFLOPS, 4)
     del q, kv, bt, sl, idx, ws, o, lse
     torch.cuda.empty_cache()
     return prob, res
 
 
 def cpu_baseline(prob):
-    """The float64 oracle on the host cores over the whole headline workload."""
-    import numpy as np
-
+    """The float64 oracle (as it stands) on the host cores: all query rows of the
+    headline workload."""
     import oracle
 
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    rows = None
     t0 = time.perf_counter()
-    oracle.problem_decode(prob, rows)
+    oracle.problem_decode(prob, None)
     dt = time.perf_counter() - t0
-    _ = np
-    return dict(value=prob.flops() / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
-                sample="all %d query rows of the headline workload (%.1f GFLOP, %.1f s)" % (
-                    prob.B * prob.s_q * prob.h_q, prob.flops() / 1e9, dt),
-                seconds=round(dt, 2), gbps=prob.bytes() / dt / 1e9)
+    return dict(value=round(prob.flops() / dt / 1e12, 5), unit="TFLOP/s", cores=threads, kind="oracle",
+                sample="all %d query rows of the headline workload (%.1f GFLOP, %.1f MB algorithmic), %.1f s" % (
+                    prob.B * prob.s_q * prob.h_q, prob.flops() / 1e9, prob.bytes() / 1e6, dt),
+                seconds=round(dt, 2), gbps=round(prob.bytes() / dt / 1e9, 3))
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the decode path here has no multi-GPU mode (run with --gpus 1)",
+              file=sys.stderr)
         sys.exit(2)
-    import torch
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    import torch  # noqa: F401
 
     import mla_paged_kv_get_amd as mla
 
     mla.lib()
-    cfgs = [int(c) for c in args.configs.split(",") if c]
-    if HEADLINE not in cfgs:
-        cfgs = [HEADLINE] + cfgs
+    listed = [int(c) for c in args.workloads.split(",") if c]
+    cfgs = listed if args.no_headline else [HEADLINE] + [c for c in listed if c != HEADLINE]
+    head = cfgs[0]
     results = {}
     head_prob = None
     for c in cfgs:
-        prob, r = measure(c, args.steps, args.warmup, args.cold)
+        prob, r = measure(c, args.steps, args.warmup)
         results[c] = r
-        print("[bench] config %d %s: decode %.1f us, %.1f TFLOP/s, %.0f GB/s (W=%d)" % (
-            c, prob.name, r["decode_ms"] * 1e3, r["tflops"], r["gbps"], r["num_workers"]), file=sys.stderr, flush=True)
-        if c == HEADLINE:
+        print("[bench] config %d %s: step %.1f us, decode kernel %.1f us (%.1f TFLOP/s, %.0f GB/s), call warm %.1f us, "
+              "cold %.1f us, scheduler %.1f us, W=%d, %d splits" % (
+                  c, prob.name, r["step_us"], r["decode_kernel_us"], r["kernel_tflops"], r["kernel_gbps"],
+                  r["decode_call_us_warm_median"], r["decode_call_us_cold_median"], r["scheduler_us"],
+                  r["num_workers"], r["splits"]), file=sys.stderr, flush=True)
+        if c == head:
             head_prob = prob
-    h = results[HEADLINE]
-    roofline = dict(bound="hbm", achieved=round(h["gbps"], 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(h["gbps"] / PEAK_HBM_GBS, 4), traffic=None,
-                    kernel="decode call (split-KV decode + combine), per-launch HIP events")
-    line = dict(metric=METRIC, value=round(head_prob.flops() / (h["step_ms"] * 1e-3) / 1e12, 2), unit="TFLOP/s",
-                n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=round(h["step_ms"], 5),
-                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
-                config=dict(workload=head_prob.name, B=head_prob.B, s_q=head_prob.s_q, h_q=head_prob.h_q,
-                            seq_len=int(head_prob.cache_seqlens[0]), block_size=64, kv="bf16"),
-                hbm_gbps=round(head_prob.bytes() / (h["step_ms"] * 1e-3) / 1e9, 1),
+    h = results[head]
+    roofline = dict(bound="hbm", achieved=h["kernel_gbps"], peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=h["kernel_frac_hbm"], traffic=measured_traffic() if head == HEADLINE else None,
+                    kernel="mla_decode_kernel (split-KV decode), mean of per-launch HIP events over the timed steps",
+                    mfma_frac=h["kernel_frac_mfma"])
+    line = dict(metric=METRIC, value=h["step_tflops"], unit="TFLOP/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(h["step_us"] / 1e3, 5), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="bf16", data="synthetic",
+                config=dict(workload=head_prob.name, B=head_prob.B, s_q=head_prob.s_q, h_q=head_prob.h_q, h_kv=1,
+                            seqlen=int(head_prob.cache_seqlens[0]), block_size=64,
+                            kv="fp8-656B" if head_prob.is_fp8 else "bf16", topk=head_prob.topk, d_qk=576, d_v=512),
+                hbm_gbps_step=round(head_prob.bytes() / (h["step_us"] * 1e-6) / 1e9, 1),
                 roofline=roofline,
-                workloads={str(c): {k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
-                           for c, r in results.items()})
+                workloads={str(c): r for c, r in results.items()})
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head_prob)
     print(json.dumps(line))

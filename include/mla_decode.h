@@ -132,6 +132,16 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
 MLA_API const char* mla_last_error(void);
 
 /*
+ * Bench hook: timing of the split-KV decode kernel alone.  While set on the
+ * calling thread (both non-NULL hipEvent_t handles created by the caller),
+ * each mla_decode_with_kvcache call records `start` on its stream right before
+ * the decode kernel and `stop` right after it, ahead of the combine launch.
+ * Passing NULL for both clears the hook.  Returns MLA_ERR_INVALID_ARG when
+ * exactly one of the two is NULL.  The events stay owned by the caller.
+ */
+MLA_API int mla_set_decode_kernel_events(void* start, void* stop);
+
+/*
  * Test hook: the FP8 -> bf16 decode the decode kernel applies, exported for
  * bit-exact checking.  tokens: device uint8 [n, 656]; out: device bf16
  * [n, 576] = the decoded 512 dims followed by the 64 RoPE dims copied verbatim.

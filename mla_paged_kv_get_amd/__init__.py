@@ -5,8 +5,8 @@ include/mla_decode.h): a scheduler kernel, a split-KV decode kernel and an lse
 combine kernel.  This package holds its sources (csrc/), its build script and a
 thin ctypes binding with the same function names.
 """
-from .binding import (Metadata, MlaError, mla_debug_dequant_fp8, mla_decode_with_kvcache, mla_get_metadata,
+from .binding import (DecodeKernelTimer, Metadata, MlaError, mla_debug_dequant_fp8, mla_decode_with_kvcache, mla_get_metadata,
                       mla_get_metadata_size, mla_last_error, lib, LIB_PATH)
 
-__all__ = ["Metadata", "MlaError", "mla_debug_dequant_fp8", "mla_decode_with_kvcache", "mla_get_metadata",
+__all__ = ["DecodeKernelTimer", "Metadata", "MlaError", "mla_debug_dequant_fp8", "mla_decode_with_kvcache", "mla_get_metadata",
            "mla_get_metadata_size", "mla_last_error", "lib", "LIB_PATH"]

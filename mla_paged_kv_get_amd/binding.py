@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
                                               Z, P, P, P]
         L.mla_debug_dequant_fp8.restype = I
         L.mla_debug_dequant_fp8.argtypes = [P, I64, P, P]
+        L.mla_set_decode_kernel_events.restype = I
+        L.mla_set_decode_kernel_events.argtypes = [P, P]
         _lib = L
     return _lib
 
@@ -101,17 +103,30 @@ class Metadata:
     topk: int
     is_fp8: bool
 
+    def total_splits(self) -> int:
+        """Number of (stream, KV range) splits in the schedule (synchronises)."""
+        return int(self.tensor[5].item())
+
 
 def mla_get_metadata(cache_seqlens: torch.Tensor, s_q: int, h_q: int, h_kv: int = 1, topk: int = 0,
-                     is_fp8: bool = False, num_workers: int = 0) -> Metadata:
-    """Run the scheduler kernel for a decode step (B = len(cache_seqlens))."""
+                     is_fp8: bool = False, num_workers: int = 0, out: Optional[torch.Tensor] = None) -> Metadata:
+    """Run the scheduler kernel for a decode step (B = len(cache_seqlens)); `out`
+    optionally supplies the int32 device buffer to fill (at least the size call's
+    metadata bytes)."""
     if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda or not cache_seqlens.is_contiguous():
         raise ValueError("cache_seqlens must be a contiguous int32 device tensor")
     B = int(cache_seqlens.numel())
     with torch.cuda.device(cache_seqlens.device):
         mb, wb, w = mla_get_metadata_size(B, s_q, h_q, h_kv, topk, num_workers)
-        meta = torch.empty(mb // 4, dtype=torch.int32, device=cache_seqlens.device)
-        _check(lib().mla_get_metadata(_ptr(cache_seqlens), B, s_q, h_q, h_kv, topk, int(is_fp8), w, _ptr(meta), mb,
+        if out is not None:
+            if out.dtype != torch.int32 or out.device != cache_seqlens.device or not out.is_contiguous() or \
+                    out.numel() * 4 < mb:
+                raise ValueError("out must be a contiguous int32 tensor of >= %d bytes on %s" % (mb, cache_seqlens.device))
+            meta = out
+        else:
+            meta = torch.empty(mb // 4, dtype=torch.int32, device=cache_seqlens.device)
+        _check(lib().mla_get_metadata(_ptr(cache_seqlens), B, s_q, h_q, h_kv, topk, int(is_fp8), w, _ptr(meta),
+                                      meta.numel() * 4,
                                       _stream(cache_seqlens.device)), "mla_get_metadata")
     return Metadata(meta, w, wb, B, s_q, h_q, h_kv, topk, bool(is_fp8))
 
@@ -179,3 +194,53 @@ def mla_debug_dequant_fp8(tokens: torch.Tensor) -> torch.Tensor:
     with torch.cuda.device(tokens.device):
         _check(lib().mla_debug_dequant_fp8(_ptr(tokens), n, _ptr(out), _stream(tokens.device)), "mla_debug_dequant_fp8")
     return out
+
+
+class DecodeKernelTimer:
+    """Bench hook: HIP events around the split-KV decode kernel alone.
+
+    Each call of `record(fn)` sets fresh start/stop events through
+    mla_set_decode_kernel_events, runs fn() (which must make exactly one
+    mla_decode_with_kvcache call on this thread) and clears the hook;
+    `durations_ms()` synchronises and returns one duration per recorded call.
+    The events come from the HIP runtime the library itself is bound to.
+    """
+
+    def __init__(self):
+        lib()  # torch's HIP runtime is loaded and shared with the library by now
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._pairs = []
+
+    def _event(self):
+        ev = ctypes.c_void_p()
+        if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise MlaError("hipEventCreate failed")
+        return ev
+
+    def record(self, fn):
+        a, b = self._event(), self._event()
+        _check(lib().mla_set_decode_kernel_events(a, b), "mla_set_decode_kernel_events")
+        try:
+            fn()
+        finally:
+            lib().mla_set_decode_kernel_events(None, None)
+        self._pairs.append((a, b))
+
+    def durations_ms(self):
+        out = []
+        for a, b in self._pairs:
+            if self._hip.hipEventSynchronize(b) != 0:
+                raise MlaError("hipEventSynchronize failed")
+            ms = ctypes.c_float()
+            if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+                raise MlaError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        for a, b in self._pairs:
+            self._hip.hipEventDestroy(a)
+            self._hip.hipEventDestroy(b)
+        self._pairs = []
+        return out

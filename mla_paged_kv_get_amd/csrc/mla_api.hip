@@ -13,6 +13,8 @@
 namespace {
 
 thread_local char g_err[512] = "";
+// bench hook: events recorded around the decode kernel (both set or both null)
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -194,10 +196,23 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
   p.n_rt = s.n_rt;
   p.W = W;
   p.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = mla::launch_decode(p, is_fp8 != 0, (hipStream_t)stream);
+  hipError_t e = hipSuccess;
+  if (g_ev_start && (e = hipEventRecord(g_ev_start, (hipStream_t)stream)) != hipSuccess)
+    return hip_fail(e, "decode start event");
+  e = mla::launch_decode(p, is_fp8 != 0, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (g_ev_stop && (e = hipEventRecord(g_ev_stop, (hipStream_t)stream)) != hipSuccess)
+    return hip_fail(e, "decode stop event");
   e = mla::launch_combine(p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MLA_OK;
+}
+
+MLA_API int mla_set_decode_kernel_events(void* start, void* stop) {
+  g_err[0] = 0;
+  if ((start == nullptr) != (stop == nullptr)) return fail(MLA_ERR_INVALID_ARG, "set both events or neither");
+  g_ev_start = (hipEvent_t)start;
+  g_ev_stop = (hipEvent_t)stop;
   return MLA_OK;
 }
 

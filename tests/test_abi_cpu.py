@@ -31,7 +31,7 @@ def L():
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     assert set(syms) == {"mla_get_metadata_size", "mla_get_metadata", "mla_decode_with_kvcache", "mla_last_error",
-                         "mla_debug_dequant_fp8"}
+                         "mla_debug_dequant_fp8", "mla_set_decode_kernel_events"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -113,3 +113,12 @@ def test_debug_dequant_rejects_bad_calls(L):
     assert f(None, ctypes.c_int64(1), ctypes.c_void_p(0x1000), None) == -1
     assert f(ctypes.c_void_p(0x1000), ctypes.c_int64(-1), ctypes.c_void_p(0x2000), None) == -1
     assert f(ctypes.c_void_p(0x1000), ctypes.c_int64(0), ctypes.c_void_p(0x2000), None) == 0  # nothing to do
+
+
+def test_decode_kernel_events_hook_needs_both_or_neither(L):
+    f = L.mla_set_decode_kernel_events
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert f(ctypes.c_void_p(0x1000), None) == -1
+    assert "both" in L.mla_last_error().decode()
+    assert f(None, ctypes.c_void_p(0x1000)) == -1
+    assert f(None, None) == 0  # clearing is always fine (no HIP call is made)
