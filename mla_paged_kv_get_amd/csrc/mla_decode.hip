@@ -77,15 +77,16 @@ constexpr float kRefRoom = 88.0f;
 constexpr int kSub = 32;                               // tokens per sub-tile
 constexpr int kSubBytes = kSub * kBf16TokenBytes;      // 36864
 constexpr int kNBuf = 3;
-constexpr int kXOffset = kNBuf * kSubBytes;            // S exchange: [2][4 waves][4][64 lanes] f32x4
+constexpr int kXOffset = kNBuf * kSubBytes;            // S exchange: [4 waves][4][64 lanes] f32x4
 constexpr int kXBytes = 4 * 64 * 16 * 4;
 // Metadata: BF16 rings int32 ring_idx[8][64], ring_pg[8][64]; FP8 int32
-// tokidx[4][32] and uint32 vmask[4] in the same space.
+// tokidx[8][32] and uint32 vmask[8] in the same space.
 constexpr int kRing = 8;
-constexpr int kMetaOffset = kXOffset + 2 * kXBytes;
+constexpr int kMetaOffset = kXOffset + kXBytes;
 constexpr int kMetaBytes = 2 * kRing * 64 * 4;
 constexpr int kFlagOffset = kMetaOffset + kMetaBytes;  // int32 per-wave flags[4]
-constexpr int kLdsBytes = kFlagOffset + 4 * 4;
+constexpr int kPOffset = kFlagOffset + 16 * 4;         // P exchange: [2 row blocks][2 k-steps][64 lanes] bf16x8
+constexpr int kLdsBytes = kPOffset + 2 * 2 * 64 * 16;
 constexpr int kBf16LoadsPerThread = kSubBytes / 16 / kThreads;  // 9
 // Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle.
 constexpr int kBufferFlags = 0x00020000;
@@ -107,8 +108,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   MLA_LDS int32_t* ring_idx = (MLA_LDS int32_t*)(smem + kMetaOffset);
   MLA_LDS int32_t* ring_pg = ring_idx + kRing * 64;
   MLA_LDS int32_t* tokidx = (MLA_LDS int32_t*)(smem + kMetaOffset);
-  MLA_LDS uint32_t* vmask = (MLA_LDS uint32_t*)(tokidx + 4 * kSub);
+  MLA_LDS uint32_t* vmask = (MLA_LDS uint32_t*)(tokidx + 8 * kSub);
   MLA_LDS int32_t* wflag = (MLA_LDS int32_t*)(smem + kFlagOffset);
+  MLA_LDS u32x4* pbuf = (MLA_LDS u32x4*)(smem + kPOffset);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
         const int tok = 16 * s2 + 8 * e4 + tl;
         const int sw = tile_swizzle(tok);
         const int sb = sw >> 2;
-        const int base = tok * kBf16TokenBytes + 8 * hf * 64 + ((cl ^ (sw & 3)) << 4) + 8 * (lane & 1);
+        const int base = tok * kBf16TokenBytes + 256 * wave + ((cl ^ (sw & 3)) << 4) + 8 * (lane & 1);
         vofs[s2][e4][0] = base + 64 * sb;
         vofs[s2][e4][1] = base - 64 * sb;
       }
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     dchunk[k] = (s - dtok[k] * kTokenChunks) ^ tile_swizzle(dtok[k]);
     doff[k] = (uint32_t)(dtok[k] * kBf16TokenBytes + dchunk[k] * 16);
   }
-  // exchange slots of this lane: [(u & 1)][wave][q4][lane]
+  // exchange slots of this lane: [wave][q4][lane]
   const int xo_base = wave * 4 * 64 + lane, xp_base = partner * 4 * 64 + lane;
 
   for (int stream = bs; stream <= es && stream < p.n_streams; ++stream) {
@@ -221,59 +223,59 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     f32x16 acc[8];
 
     // ---- per sub-tile metadata ----------------------------------------------------
-    // Whatever a round needs to know about a later sub-tile (its cache page, or
-    // the token rows of its 32 index slots) is fetched rounds ahead into LDS, so
-    // no round waits on a global load it has just issued.
+    // Round u (below) streams sub-tile u + 2 into LDS; whatever it needs to know
+    // about a sub-tile (its cache page, or the token rows of its 32 index slots)
+    // was fetched rounds ahead into LDS, so no round waits on a load it just issued.
     //
     // BF16 (tiles arrive by direct global->LDS loads): the metadata travels the
-    // same way, into rings of 8 sub-tiles.  Round u fetches the page of sub-tile
-    // u + 4 (dense) or the indices of sub-tile u + 6 and the pages of sub-tile
-    // u + 4's indices (sparse).  A direct load issued in round r has landed once
-    // round r + 1 ends, so every wave sees it from round r + 2 on; round u stages
-    // sub-tile u + 2.  No loaded value ever lands in a register here: the
+    // same way, into rings of 8 sub-tiles, issued at the start of a round and
+    // landed by its end.  Round u fetches the page of sub-tile u + 3 (dense), or
+    // the indices of sub-tile u + 4 and the pages of sub-tile u + 3's indices
+    // (sparse).  No loaded value ever lands in a register inside the loop: the
     // compiler could only wait for such a value by draining every direct load
     // still streaming.
     //
     // FP8 (tiles go through registers): sub-tile u's metadata sits in LDS slot
-    // u & 3 (dense: its page; sparse: the token row of each slot, -1 when not
+    // u & 7 (dense: its page; sparse: the token row of each slot, -1 when not
     // attended, and the attended mask); every wave loads the metadata of sub-tile
-    // u + 3 during round u and wave 0 publishes it at the end of the round.
+    // u + 4 during round u and wave 0 publishes it at the end of the round.
     auto slot_ok = [&](int u) { return u < u1 && u * kSub + l32 < p.topk; };  // sparse slot l32 exists
     // BF16 direct metadata loads (64 lanes each; lanes 32..63 repeat 0..31)
     auto meta_dma = [&](int u) {
       if constexpr (SPARSE) {
-        // indices of sub-tile u + 6
-        const int si = min((u + 6) * kSub + l32, p.topk - 1);
+        // indices of sub-tile u + 4
+        const int si = min((u + 4) * kSub + l32, p.topk - 1);
         __builtin_amdgcn_global_load_lds((const void*)(idx_row + si),
-                                         (MLA_LDS void*)(ring_idx + ((u + 6) & (kRing - 1)) * 64), 4, 0, 0);
-        // pages of sub-tile u + 4's indices
-        const int idx = ring_idx[((u + 4) & (kRing - 1)) * 64 + l32];
-        const bool ok = slot_ok(u + 4) && idx >= 0;
+                                         (MLA_LDS void*)(ring_idx + ((u + 4) & (kRing - 1)) * 64), 4, 0, 0);
+        // pages of sub-tile u + 3's indices
+        const int idx = ring_idx[((u + 3) & (kRing - 1)) * 64 + l32];
+        const bool ok = slot_ok(u + 3) && idx >= 0;
         __builtin_amdgcn_global_load_lds((const void*)(bt_row + (ok ? idx >> 6 : 0)),
-                                         (MLA_LDS void*)(ring_pg + ((u + 4) & (kRing - 1)) * 64), 4, 0, 0);
+                                         (MLA_LDS void*)(ring_pg + ((u + 3) & (kRing - 1)) * 64), 4, 0, 0);
       } else {
-        // page of sub-tile u + 4 (the split's last page past its end)
-        buffer_load_lds4(bt_rs, (MLA_LDS void*)(ring_pg + ((u + 4) & (kRing - 1)) * 64),
-                         (uint32_t)(min(u + 4, u1 - 1) >> 1) * 4u);
+        // page of sub-tile u + 3 (the split's last page past its end)
+        buffer_load_lds4(bt_rs, (MLA_LDS void*)(ring_pg + ((u + 3) & (kRing - 1)) * 64),
+                         (uint32_t)(min(u + 3, u1 - 1) >> 1) * 4u);
       }
     };
-    // BF16 prologue: the same ring entries by plain loads (rings for u0 .. u0 + 5)
+    // BF16 prologue: the same ring entries by plain loads (indices of u0 .. u0 + 3,
+    // pages of u0 .. u0 + 2)
     auto meta_fill = [&]() {
       if (wave == 0) {
         if constexpr (SPARSE) {
 #pragma unroll
-          for (int j = 0; j < 6; ++j) {
+          for (int j = 0; j < 4; ++j) {
             const int u = u0 + j;
             const int idx = idx_row[min(u * kSub + l32, p.topk - 1)];
             ring_idx[(u & (kRing - 1)) * 64 + lane] = idx;
-            if (j < 4) {
+            if (j < 3) {
               const bool ok = slot_ok(u) && idx >= 0;
               ring_pg[(u & (kRing - 1)) * 64 + lane] = bt_row[ok ? idx >> 6 : 0];
             }
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < 3; ++j) {
             const int u = u0 + j;
             ring_pg[(u & (kRing - 1)) * 64 + lane] = bt_row[min(u, u1 - 1) >> 1];
           }
@@ -290,16 +292,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     auto publish = [&](int u, int v) {  // wave 0
       if (SPARSE) {
         const uint64_t m = __ballot(v >= 0);
-        if (lane < kSub) tokidx[(u & 3) * kSub + lane] = v;
-        if (lane == 0) vmask[u & 3] = (uint32_t)m;
+        if (lane < kSub) tokidx[(u & 7) * kSub + lane] = v;
+        if (lane == 0) vmask[u & 7] = (uint32_t)m;
       } else if (lane == 0) {
-        tokidx[(u & 3) * kSub] = v;
+        tokidx[(u & 7) * kSub] = v;
       }
     };
     // attended mask of sub-tile u's 32 slots (sparse)
     auto sparse_mask = [&](int u) -> uint32_t {
       if constexpr (FP8) {
-        return vmask[u & 3];
+        return vmask[u & 7];
       } else {
         const bool ok = slot_ok(u) && ring_idx[(u & (kRing - 1)) * 64 + l32] >= 0;
         return (uint32_t)__ballot(ok);
@@ -310,11 +312,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     // FP8: byte address of stored token t of sub-tile u (the zero token when not attended)
     auto token_ptr = [&](int u, int t) -> const uint8_t* {
       if (SPARSE) {
-        const int tok = tokidx[(u & 3) * kSub + t];
+        const int tok = tokidx[(u & 7) * kSub + t];
         return tok >= 0 ? p.kv + (int64_t)tok * tok_bytes : g_zero_token;
       }
       if (u * kSub + t >= seqlen) return g_zero_token;
-      const int page = tokidx[(u & 3) * kSub];
+      const int page = tokidx[(u & 7) * kSub];
       return p.kv + ((int64_t)page * kPage + (u & 1) * kSub + t) * tok_bytes;
     };
     // BF16 direct loads of sub-tile u: this thread's nine 16-byte pieces.  Dense
@@ -343,9 +345,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
         const int page = __builtin_amdgcn_readfirstlane(ring_pg[r]);
         const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
         L.rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, kSubBytes, kBufferFlags);
-        const int valid = seqlen - u * kSub;  // tokens of the sub-tile inside the sequence
+        if ((u + 1) * kSub <= seqlen) {
 #pragma unroll
-        for (int k = 0; k < kBf16LoadsPerThread; ++k) L.voff[k] = dtok[k] < valid ? doff[k] : (uint32_t)kSubBytes;
+          for (int k = 0; k < kBf16LoadsPerThread; ++k) L.voff[k] = doff[k];
+        } else {
+          asm volatile("");  // a real branch: only the last sub-tile pays for this
+          const int valid = seqlen - u * kSub;  // tokens of the sub-tile inside the sequence
+#pragma unroll
+          for (int k = 0; k < kBf16LoadsPerThread; ++k) L.voff[k] = dtok[k] < valid ? doff[k] : (uint32_t)kSubBytes;
+        }
       }
     };
     auto stage_issue = [&](const Bf16Loads& L, int k, MLA_LDS char* buf) {
@@ -381,6 +389,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       }
       *(MLA_LDS u32x4*)(buf + tile_slot(t, 64 + j) * 16) = r.r;
     };
+    // ---- score exchange and PV pieces ---------------------------------------------
+    // The pair adds its two partial S^T blocks through LDS: slots [wave][q4][lane].
+    MLA_LDS f32x4* xo = xbuf + xo_base;
+    MLA_LDS f32x4* xp = xbuf + xp_base;
+    auto kread = [&](MLA_LDS char* kb, int kk) -> bf16x8 {
+      const int off = kk < 16 ? kofs[kk & 3] + (kk >> 2) * 128 : kofs_r[kk - 16];
+      return *(MLA_LDS bf16x8*)(kb + off);
+    };
+    // V^T fragment (this wave's 32-column block cb of its 128 columns, 16-token k-step s2)
+    auto vread = [&](MLA_LDS char* vb, int s2, int cb) -> bf16x8 {
+      const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(vb + vofs[s2][0][cb & 1] + 64 * cb));
+      const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(vb + vofs[s2][1][cb & 1] + 64 * cb));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 
     // Reference maximum m_ref (log2 domain, per row): the row's first finite
     // sub-tile maximum + kRefLift, fixed for the whole split, so P = 2^(x - m_ref)
@@ -400,122 +422,79 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       if (redo) m_ref = m_seen + kRefLift;
       bool overflow = false;
 
-      // ---- prologue: metadata, then stage u0 and u0 + 1 ----------------------------
+      // ---- prologue: metadata, sub-tiles u0 and u0 + 1 in LDS, S of u0 ------------
       int idx_pref = -1;  // FP8 sparse: index of slot l32 of sub-tile u + 4
-      RawFp8 raw;         // FP8: sub-tile u + 1 in flight in VGPRs
+      RawFp8 raw;         // FP8: sub-tile u + 2 in flight in VGPRs
       if constexpr (FP8) {
-        int v0, v1, v2;
-        if (SPARSE) {
-          v0 = tok_of(idx_at(u0));
-          v1 = tok_of(idx_at(u0 + 1));
-          v2 = tok_of(idx_at(u0 + 2));
-          idx_pref = idx_at(u0 + 3);
-        } else {
-          v0 = page_load(u0);
-          v1 = page_load(u0 + 1);
-          v2 = page_load(u0 + 2);
-        }
-        if (wave == 0) {
-          publish(u0, v0);
-          publish(u0 + 1, v1);
-          publish(u0 + 2, v2);
-        }
+        int v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = SPARSE ? tok_of(idx_at(u0 + j)) : page_load(u0 + j);
+        if (SPARSE) idx_pref = idx_at(u0 + 4);
+        if (wave == 0)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) publish(u0 + j, v[j]);
         __syncthreads();
         load_fp8(u0, raw);
         store_fp8(raw, buffer(u0));
         load_fp8(u0 + 1, raw);
+        store_fp8(raw, buffer(u0 + 1));
+        load_fp8(u0 + 2, raw);
         __syncthreads();
       } else {
         meta_fill();
         __syncthreads();
         stage_bf16(u0, buffer(u0));
         stage_bf16(u0 + 1, buffer(u0 + 1));
-        tile_barrier_keep<kBf16LoadsPerThread>();  // sub-tile u0 has landed
+        tile_barrier_drain();
+      }
+      float x[16];  // full scores S^T of the sub-tile whose softmax comes next
+      {
+        MLA_LDS char* kb = buffer(u0);
+        f32x16 s = {};
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kb, kk), qf[kk], s, 0, 0, 0);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) xo[q4 * 64] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+        lds_barrier();
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 o = xp[q4 * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * q4 + e] = hf == 0 ? s[4 * q4 + e] + o[e] : o[e] + s[4 * q4 + e];
+        }
       }
 
-      float x[16];
-      // One round: compute sub-tile u from buf while filling nxt (FP8: sub-tile
-      // u + 1 from registers; BF16: sub-tile u + 2 by direct loads).  The two
-      // buffers are distinct, and saying so (restrict) lets the compiler keep the
-      // direct loads in flight across the reads of buf.
-      auto round = [&](const int u, MLA_LDS char* __restrict__ buf,
+      // One round u: PV of sub-tile u (buffer vb) and QK of sub-tile u + 1 (kb),
+      // whose MFMAs run under u's softmax, while sub-tile u + 2 streams into nxt.
+      // The buffers are distinct, and saying so (restrict) lets the compiler keep
+      // the direct loads in flight across the reads of vb and kb.
+      auto round = [&](const int u, MLA_LDS char* __restrict__ vb, MLA_LDS char* __restrict__ kb,
                        MLA_LDS char* __restrict__ nxt) __attribute__((always_inline)) {
-        int meta = 0;  // FP8: metadata of sub-tile u + 3 (published at the end of this round)
+        // ---- phase A: metadata, streaming, QK(u + 1) under softmax(u) ---------------
+        int meta = 0;  // FP8: metadata of sub-tile u + 4 (published at the end of this round)
         if constexpr (FP8) {
           if (SPARSE) {
             meta = tok_of(idx_pref);
-            idx_pref = idx_at(u + 4);
+            idx_pref = idx_at(u + 5);
           } else {
-            meta = page_load(u + 3);
+            meta = page_load(u + 4);
           }
         } else {
           meta_dma(u);
         }
         __builtin_amdgcn_sched_barrier(0);  // metadata loads stay ahead of the tile loads
-        // stream sub-tile u + 2 (its buffer was freed by the barrier ending round u - 1):
-        // FP8 converts the registers loaded last round and loads the next; BF16
-        // prepares its nine direct loads here and issues them between the QK MFMAs
         Bf16Loads L;
         if constexpr (FP8) {
-          store_fp8(raw, nxt);  // sub-tile u + 1 arrived during the last round
-          load_fp8(u + 2, raw);
+          store_fp8(raw, nxt);  // sub-tile u + 2 arrived during the last round
+          load_fp8(u + 3, raw);
         } else {
           stage_prep(u + 2, L);
         }
-        // partial S^T over this wave's dims.  Issue order is pinned (a scheduling
-        // barrier per step): the K fragments are read six MFMAs ahead, so the LDS
-        // reads overlap the MFMA chain.
-        constexpr int kAhead = 6;
-        bf16x8 kf[18];
-        auto kread = [&](int kk) {
-          const int off = kk < 16 ? kofs[kk & 3] + (kk >> 2) * 128 : kofs_r[kk - 16];
-          kf[kk] = *(MLA_LDS bf16x8*)(buf + off);
-        };
-#pragma unroll
-        for (int kk = 0; kk < kAhead; ++kk) kread(kk);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 s = {};
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-          if (kk + kAhead < 18) kread(kk + kAhead);
-          if constexpr (!FP8) {
-            if (kk < kBf16LoadsPerThread) stage_issue(L, kk, nxt);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // swap partial scores with the partner wave
-        MLA_LDS f32x4* xo = xbuf + (u & 1) * (4 * 4 * 64) + xo_base;
-        MLA_LDS f32x4* xp = xbuf + (u & 1) * (4 * 4 * 64) + xp_base;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) xo[q4 * 64] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-        lds_barrier();
-        f32x4 xr[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) xr[q4] = xp[q4 * 64];
-        // V^T fragments of the first 16 tokens do not depend on P: they are read
-        // while the softmax runs
-        auto vread = [&](int s2, int cb) -> bf16x8 {
-          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][0][cb & 1] + 64 * cb));
-          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(buf + vofs[s2][1][cb & 1] + 64 * cb));
-          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-        bf16x8 va0[8];
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) va0[cb] = vread(0, cb);
-        __builtin_amdgcn_sched_barrier(0);
-        // raw scores S = (hf 0 partial) + (hf 1 partial), the same sum in both waves
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float mine = s[4 * q4 + e], theirs = xr[q4][e];
-            x[4 * q4 + e] = hf == 0 ? mine + theirs : theirs + mine;
-          }
-        // mask: lane holds row l32, tokens 8 (e / 4) + 4 h + e % 4
+        // mask of sub-tile u: lane holds row l32, tokens 8 (e / 4) + 4 h + e % 4
         const uint32_t tmask = SPARSE ? sparse_mask(u) : 0u;
         const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= seqlen;
         if (!full) {
+          asm volatile("");  // a real branch: full sub-tiles skip the masking
           const int vcount = seqlen - u * kSub;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
@@ -524,87 +503,159 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
             x[e] = ok ? x[e] : kNegInf;
           }
         }
-        // row maximum in the log2 domain (the scale is positive)
-        float mx = x[0];
+        // The issue order is pinned (a scheduling barrier per step): MFMA kk of
+        // QK(u + 1), the K fragment six steps ahead, one of the nine tile loads,
+        // then a slice of u's softmax.  Softmax: row maximum (log2 domain, the
+        // scale is positive), reference update, then P = 2^(scale_log2 S - m_ref)
+        // for this wave's k-step (the pair splits the exponentials: the hf wave
+        // takes tokens 16 hf .. 16 hf + 15, its x[8 hf ..]).
+        constexpr int kAhead = 6;
+        bf16x8 kf[18];
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
-        m_seen = fmaxf(m_seen, mx);
-        if (m_ref == kNegInf && mx != kNegInf) m_ref = mx + kRefLift;
-        overflow |= mx > m_ref + kRefRoom;
-
-        // P = 2^(scale_log2 S - m_ref) and O^T += V^T P^T over two 16-token k-steps
-        const float msafe = m_ref == kNegInf ? 0.f : m_ref;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], p.scale_log2, -msafe));
-          l_sum += x[e];
-        }
-        bf16x8 pb0, pb1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb0[e] = (__bf16)x[e];
-          pb1[e] = (__bf16)x[8 + e];
-        }
+        for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kb, kk);
         __builtin_amdgcn_sched_barrier(0);
-        // second 16 tokens' V^T reads interleaved with the first 16 tokens' MFMAs
-        bf16x8 va1[8];
+        f32x16 s = {};
+        float m4[4], mx = 0.f, msafe = 0.f;
+        float xs[8];
+        bf16x8 pown;
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0[cb], pb0, acc[cb], 0, 0, 0);
-          va1[cb] = vread(1, cb);
+        for (int kk = 0; kk < 18; ++kk) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+          if (kk + kAhead < 18) kf[kk + kAhead] = kread(kb, kk + kAhead);
+          if constexpr (!FP8) {
+            if (kk < kBf16LoadsPerThread) stage_issue(L, kk, nxt);
+          }
+          if (kk < 4) {
+            m4[kk] = fmaxf(fmaxf(x[4 * kk], x[4 * kk + 1]), fmaxf(x[4 * kk + 2], x[4 * kk + 3]));
+          } else if (kk == 4) {
+            mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+            // lanes l and l ^ 32 hold the same row (a VALU lane swap, no LDS)
+            mx = halves_max(mx) * p.scale_log2;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xs[e] = hf == 0 ? x[e] : x[8 + e];
+          } else if (kk == 5) {
+            m_seen = fmaxf(m_seen, mx);
+            if (m_ref == kNegInf && mx != kNegInf) m_ref = mx + kRefLift;
+            overflow |= mx > m_ref + kRefRoom;
+            msafe = m_ref == kNegInf ? 0.f : m_ref;
+          } else if (kk < 14) {
+            const int e = kk - 6;
+            const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[e], p.scale_log2, -msafe));
+            l_sum += pe;
+            pown[e] = (__bf16)pe;
+          } else if (kk == 14) {
+            pbuf[(rb * 2 + hf) * 64 + lane] = __builtin_bit_cast(u32x4, pown);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
+        lds_barrier();  // every P block of sub-tile u is in LDS
+
+        // ---- phase B: O^T += V^T P^T for sub-tile u ----------------------------------
+        const bf16x8 pb0 = __builtin_bit_cast(bf16x8, pbuf[(rb * 2 + 0) * 64 + lane]);
+        const bf16x8 pb1 = __builtin_bit_cast(bf16x8, pbuf[(rb * 2 + 1) * 64 + lane]);
+        const bf16x8 qb0 = __builtin_bit_cast(bf16x8, pbuf[((rb ^ 1) * 2 + 0) * 64 + lane]);
+        const bf16x8 qb1 = __builtin_bit_cast(bf16x8, pbuf[((rb ^ 1) * 2 + 1) * 64 + lane]);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 va[2][4];
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1[cb], pb1, acc[cb], 0, 0, 0);
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) va[s2][cb] = vread(vb, s2, cb);
+        __builtin_amdgcn_sched_barrier(0);
+        // acc[0..3]: rows of this wave's row block, acc[4..7]: the other row block;
+        // columns 128 wave + 32 cb
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s2][cb], s2 ? pb1 : pb0, acc[cb], 0, 0, 0);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            acc[4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s2][cb], s2 ? qb1 : qb0, acc[4 + cb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the PV MFMAs issue before the round's last waits
+        // partial S^T of sub-tile u + 1 to the partner
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) xo[q4 * 64] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
         if constexpr (FP8) {
-          if (wave == 0) publish(u + 3, meta);
-          lds_barrier();  // sub-tile u + 1 went through registers; u + 2 stays in flight
+          if (wave == 0) publish(u + 4, meta);
+          lds_barrier();  // sub-tile u + 2 went through registers
         } else {
-          // this round's direct loads may still fly; everything before has landed
-          tile_barrier_keep<kBf16LoadsPerThread + (SPARSE ? 2 : 1)>();
+          tile_barrier_drain();  // sub-tile u + 2 and the metadata have landed
+        }
+        // ---- phase C: S of sub-tile u + 1 = (hf 0 partial) + (hf 1 partial) ----------
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 o = xp[q4 * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * q4 + e] = hf == 0 ? s[4 * q4 + e] + o[e] : o[e] + s[4 * q4 + e];
         }
       };
-      for (int u = u0; u < u1; ++u) round(u, buffer(u), buffer(u + (FP8 ? 1 : 2)));
-      // tiles staged past the end are still in flight: let them land before LDS is reused
+      for (int u = u0; u < u1; ++u) round(u, buffer(u), buffer(u + 1), buffer(u + 2));
+      // the last round streamed sub-tiles past the end: let them land before LDS is reused
       tile_barrier_drain();
 
-      // the restart must be taken by the whole workgroup (it contains barriers)
-      if (lane == 0) wflag[wave] = __ballot(overflow) != 0 ? 1 : 0;
+      // the restart must be taken by the whole workgroup (it contains barriers);
+      // the vote is over every lane, so it is taken before the lane-0 store
+      const bool wave_overflow = __ballot(overflow) != 0;
+      if (lane == 0) wflag[wave] = wave_overflow ? 1 : 0;
       __syncthreads();
       redo = (wflag[0] | wflag[1] | wflag[2] | wflag[3]) != 0;
       __syncthreads();
     } while (redo);
 
     // ---- epilogue -------------------------------------------------------------------
+    // This wave holds O^T for both row blocks (columns 128 wave ..); each row's
+    // l and reference come from the pair that owns the row.
     l_sum += __shfl_xor(l_sum, 32);
-    const bool empty = !(l_sum > 0.f);
-    const float inv = empty ? 0.f : 1.f / l_sum;
-    const float lse_v = empty ? kNegInf : (m_ref + __log2f(l_sum)) * 0.69314718055994531f;
-    if (row_ok) {
-      if (final_out) {
-        uint16_t* orow = p.o + (row_base + row) * kDV + 256 * hf + 4 * h;
+    {
+      // l[row block][k-step][32] (each wave summed its k-step), then m_ref[64]
+      MLA_LDS float* lm = (MLA_LDS float*)(smem + kXOffset);
+      if (h == 0) {
+        lm[(rb * 2 + hf) * 32 + l32] = l_sum;
+        if (hf == 0) lm[128 + rb * 32 + l32] = m_ref;
+      }
+      __syncthreads();
+      const float l_own = lm[(rb * 2) * 32 + l32] + lm[(rb * 2 + 1) * 32 + l32];
+      const float l_oth = lm[((rb ^ 1) * 2) * 32 + l32] + lm[((rb ^ 1) * 2 + 1) * 32 + l32];
+      const float m_oth = lm[128 + (rb ^ 1) * 32 + l32];
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
+      for (int j = 0; j < 2; ++j) {
+        const float lj = j == 0 ? l_own : l_oth, mj = j == 0 ? m_ref : m_oth;
+        const int rowj = rt * 64 + (rb ^ j) * kWaveRows + l32;
+        const bool empty = !(lj > 0.f);
+        const float inv = empty ? 0.f : 1.f / lj;
+        const float lse_v = empty ? kNegInf : (mj + __log2f(lj)) * 0.69314718055994531f;
+        if (rowj < p.R_stream) {
+          if (final_out) {
+            uint16_t* orow = p.o + (row_base + rowj) * kDV + 128 * wave + 4 * h;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            bf16x2 v0, v1;
-            v0.x = (__bf16)(acc[cb][4 * i + 0] * inv);
-            v0.y = (__bf16)(acc[cb][4 * i + 1] * inv);
-            v1.x = (__bf16)(acc[cb][4 * i + 2] * inv);
-            v1.y = (__bf16)(acc[cb][4 * i + 3] * inv);
-            *(u32x2*)(orow + cb * 32 + 8 * i) = u32x2{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1)};
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const f32x16& a = acc[4 * j + cb];
+                bf16x2 v0, v1;
+                v0.x = (__bf16)(a[4 * i + 0] * inv);
+                v0.y = (__bf16)(a[4 * i + 1] * inv);
+                v1.x = (__bf16)(a[4 * i + 2] * inv);
+                v1.y = (__bf16)(a[4 * i + 3] * inv);
+                *(u32x2*)(orow + cb * 32 + 8 * i) =
+                    u32x2{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1)};
+              }
+            if (j == 0 && h == 0 && hf == 0) p.lse[row_base + rowj] = lse_v;
+          } else {
+            float* prow = p.part_o + ((int64_t)sid * p.R_stream + rowj) * kDV + 128 * wave + 4 * h;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const f32x16& a = acc[4 * j + cb];
+                *(f32x4*)(prow + cb * 32 + 8 * i) =
+                    f32x4{a[4 * i] * inv, a[4 * i + 1] * inv, a[4 * i + 2] * inv, a[4 * i + 3] * inv};
+              }
+            if (j == 0 && h == 0 && hf == 0) p.part_lse[(int64_t)sid * p.R_stream + rowj] = lse_v;
           }
-        if (h == 0 && hf == 0) p.lse[row_base + row] = lse_v;
-      } else {
-        float* prow = p.part_o + ((int64_t)sid * p.R_stream + row) * kDV + 256 * hf + 4 * h;
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *(f32x4*)(prow + cb * 32 + 8 * i) = f32x4{acc[cb][4 * i] * inv, acc[cb][4 * i + 1] * inv,
-                                                     acc[cb][4 * i + 2] * inv, acc[cb][4 * i + 3] * inv};
-        if (h == 0 && hf == 0) p.part_lse[(int64_t)sid * p.R_stream + row] = lse_v;
+        }
       }
     }
     __syncthreads();  // LDS is reused by the next piece

@@ -52,6 +52,17 @@ __device__ __forceinline__ void dequant16(u32x4 codes, float scale, u32x4& lo, u
   hi = u32x4{c.x, c.y, d.x, d.y};
 }
 
+// max(v of lane l, v of lane l ^ 32): v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second, so with both
+// operands = v each lane ends up holding its own value and its partner's.
+// Inline asm because this compiler's builtin for the swap hands back the wrong
+// register for one of its two results (checked on gfx950: half the lanes wrong).
+__device__ __forceinline__ float halves_max(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 __device__ __forceinline__ float pick_scale(const u32x4& s, int i) {
   const uint32_t v = i == 0 ? s.x : i == 1 ? s.y : i == 2 ? s.z : s.w;
   return __builtin_bit_cast(float, v);

@@ -216,6 +216,18 @@ def test_metadata_reused_across_calls():
         compare(o, l, o_ref, lse_ref, "call %d with shared metadata" % call)
 
 
+@pytest.mark.parametrize("is_fp8,topk,scale", [(False, 0, 4.0), (True, 0, 4.0), (False, 256, 4.0), (True, 256, 4.0)])
+def test_large_score_spread(is_fp8, topk, scale):
+    """Scores spread over hundreds of natural-log units: later tokens overflow the
+    first sub-tile's reference, so the split must be recomputed with the true
+    maximum, which in turn must be taken over every token of each row."""
+    kw = dict(seed=95, is_fp8=is_fp8, softmax_scale=scale)
+    if topk:
+        kw.update(topk=topk, n_invalid=7)
+    prob = mi.make_problem("large spread", 2, 1, 128, [2000, 700], **kw)
+    check_problem(prob, num_workers=3)
+
+
 def test_lse_merge_through_the_abi():
     """Two calls over the two halves of each index list, merged with the oracle's
     lse rule, equal one call over the whole list."""
