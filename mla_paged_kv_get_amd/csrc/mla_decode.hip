@@ -8,31 +8,33 @@
 // final o and lse here, otherwise each split leaves a normalised partial o and
 // its lse for the combine kernel (same page, scheduling and combine sections).
 //
-// Mapping to the hardware.  One workgroup (4 waves, one per SIMD) owns 64 query
-// rows of one stream; the chip runs one such workgroup per compute unit.  Waves
-// 2 r and 2 r + 1 ... are paired as (row block rb = wave & 1, half hf =
-// wave >> 1): both waves of a pair own the same 32 rows; the hf wave keeps half
-// of the Q dims in VGPRs (dims 256 hf .. + 256 and 512 + 32 hf .. + 32, 18 bf16x8
-// fragments) and half of the O^T columns (256 hf .. + 256) in AGPRs.
+// Mapping to the hardware.  One workgroup of 8 waves (two per SIMD) owns 64
+// query rows of one stream; the chip runs one such workgroup per compute unit.
+// Two waves per SIMD matter here: a wave's LDS reads and writes are issued at a
+// fixed per-wave rate, so the second wave doubles the LDS traffic a SIMD can
+// sustain, and each wave's waits (LDS, barrier) are covered by the other's MFMAs.
 // Per 32-token sub-tile of the KV stream:
-//   1. the page's bf16 rows are staged in a swizzled LDS tile (BF16: direct
+//   1. the sub-tile's bf16 rows are staged in a swizzled LDS tile (BF16: direct
 //      global->LDS 16-byte loads; FP8: 16-byte loads into VGPRs, e4m3 -> fp32
-//      (exact) * scale (RNE) -> bf16 (RNE), then LDS); three buffers keep two
-//      sub-tiles in flight behind the one being computed;
-//   2. each wave computes its partial S^T = K Q^T over its half of the dims on
-//      v_mfma_f32_32x32x16_bf16 (the K tile is the A operand), the pair swaps the
-//      partials through LDS and both add them in the same order, so both hold the
-//      same scores;
-//   3. softmax in the log2 domain, lane-local (S^T puts query row lane % 32 in
-//      every lane's accumulator column) against a per-row reference fixed at the
-//      first scores of the split (see the main loop), so O and l need no
-//      rescaling and O is touched only by MFMAs;
-//   4. O^T += V^T P^T on the same MFMA: P goes from the score registers straight
-//      into the B operand, V^T comes from the token-major tile through
-//      ds_read_b64_tr_b16.
-// Tokens that no row attends (page tails, -1 indices) are loaded from a static
-// zero token, so every wave issues the same number of loads per sub-tile and
-// their scores are masked to -inf.
+//      (exact) * scale (RNE) -> bf16 (RNE), then LDS); four buffers hold the
+//      sub-tile being multiplied by V, the next one (whose scores are being
+//      computed) and the two behind it;
+//   2. scores: wave w computes S^T for 16 query rows (16 (w & 3) ..) and 16 tokens
+//      (16 (w >> 2) ..) over all 576 dims on v_mfma_f32_16x16x32_bf16, with its Q
+//      rows in VGPRs, so no wave needs another's partial scores;
+//   3. softmax in the log2 domain against a per-row reference fixed at the start
+//      of the split (see the main loop), so O and l need no rescaling; each wave
+//      writes its 16 x 16 bf16 P block to LDS;
+//   4. O^T += V^T P^T on v_mfma_f32_32x32x16_bf16: wave w owns O columns
+//      64 w .. 64 w + 63 for all 64 rows, reading P of the whole sub-tile from LDS
+//      and V^T from the token-major tile through ds_read_b64_tr_b16.
+// The steps are pipelined one sub-tile apart: round u computes the softmax of
+// sub-tile u, then O += P V of sub-tile u - 1 (whose P every wave wrote in the
+// previous round), then the scores of sub-tile u + 1, while sub-tile u + 2
+// streams in; one workgroup barrier per round publishes all of it.
+// Tokens that no row attends (page tails, -1 indices) are loaded as zeros, so
+// every wave issues the same loads per sub-tile and their scores are masked
+// to -inf.
 #include "mla_device.hpp"
 
 namespace mla {
@@ -42,21 +44,14 @@ __device__ __attribute__((aligned(64))) uint8_t g_zero_token[kBf16TokenBytes] = 
 
 namespace {
 
+constexpr int kDecThreads = 512;  // 8 waves
+
 // Workgroup barrier that orders LDS traffic only.  __syncthreads() implies a
-// release fence that also waits for every outstanding global->LDS load, which
-// would drain the tiles streaming ahead; these barriers leave them in flight.
-// The memory clobber keeps the compiler from moving memory accesses across.
+// release fence that also waits for every outstanding global->LDS load; this one
+// leaves them in flight.  The memory clobber keeps the compiler from moving
+// memory accesses across.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Also wait until at most N global->LDS loads of this wave are outstanding:
-// with N = the loads one round issues, everything issued before this round has
-// landed (the hardware completes these loads in order).
-template <int N>
-__device__ __forceinline__ void tile_barrier_keep() {
-  static_assert(N == 9 || N == 10 || N == 11, "unexpected load count");
-  if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if constexpr (N == 11) asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
+// Also wait for every global->LDS load of this wave.
 __device__ __forceinline__ void tile_barrier_drain() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -67,6 +62,9 @@ __device__ __forceinline__ void tile_barrier_drain() {
 __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, MLA_LDS void* dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
 }
+__device__ __forceinline__ void global_load_lds16(const void* src, MLA_LDS void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
 __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t rs, MLA_LDS void* dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
 }
@@ -76,50 +74,56 @@ constexpr float kRefLift = 32.0f;   // log2 units
 constexpr float kRefRoom = 88.0f;
 constexpr int kSub = 32;                               // tokens per sub-tile
 constexpr int kSubBytes = kSub * kBf16TokenBytes;      // 36864
-constexpr int kNBuf = 3;
-constexpr int kXOffset = kNBuf * kSubBytes;            // S exchange: [4 waves][4][64 lanes] f32x4
-constexpr int kXBytes = 4 * 64 * 16 * 4;
+constexpr int kNBuf = 4;
+// P exchange: [2 (sub-tile parity)][2 row blocks][2 k-steps][64 lanes] bf16x8
+constexpr int kPOffset = kNBuf * kSubBytes;
+constexpr int kPHalf = 2 * 2 * 64 * 16;
 // Metadata: BF16 rings int32 ring_idx[8][64], ring_pg[8][64]; FP8 int32
 // tokidx[8][32] and uint32 vmask[8] in the same space.
 constexpr int kRing = 8;
-constexpr int kMetaOffset = kXOffset + kXBytes;
+constexpr int kMetaOffset = kPOffset + 2 * kPHalf;
 constexpr int kMetaBytes = 2 * kRing * 64 * 4;
-constexpr int kFlagOffset = kMetaOffset + kMetaBytes;  // int32 per-wave flags[4]
-constexpr int kPOffset = kFlagOffset + 16 * 4;         // P exchange: [2 row blocks][2 k-steps][64 lanes] bf16x8
-constexpr int kLdsBytes = kPOffset + 2 * 2 * 64 * 16;
-constexpr int kBf16LoadsPerThread = kSubBytes / 16 / kThreads;  // 9
+constexpr int kFlagOffset = kMetaOffset + kMetaBytes;  // int32 per-wave flags[8]
+constexpr int kXOffset = kFlagOffset + 64;             // float row exchange [3][64]
+constexpr int kLdsBytes = kXOffset + 3 * 64 * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+// BF16 staging: 2304 16-byte slots per sub-tile; thread tid fills slots
+// 512 k + tid (k < 4) and, for tid < 256, 2048 + tid.
+constexpr int kSlots = kSubBytes / 16;
+constexpr int kLoads = 5;
+static_assert(kSlots == 4 * kDecThreads + kDecThreads / 2, "staging split");
 // Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle.
 constexpr int kBufferFlags = 0x00020000;
 
-// FP8 registers of one sub-tile for this thread: token tid / 8, code chunks
-// j + 8 i (i = 0..3, j = tid % 8; chunk i uses scale i), the four scales and
-// RoPE chunk j.
+// FP8 registers of one sub-tile for this thread: token tid / 16, code chunks
+// j and j + 16 (j = tid % 16; chunk c uses scale c / 8), the four scales and
+// RoPE chunk j % 8 (stored by j < 8).
 struct RawFp8 {
-  u32x4 v[4];
+  u32x4 v[2];
   u32x4 sc;
   u32x4 r;
 };
 
 template <bool FP8, bool SPARSE>
-__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
-  MLA_LDS f32x4* xbuf = (MLA_LDS f32x4*)(smem + kXOffset);
+  MLA_LDS char* pbuf = smem + kPOffset;
   MLA_LDS int32_t* ring_idx = (MLA_LDS int32_t*)(smem + kMetaOffset);
   MLA_LDS int32_t* ring_pg = ring_idx + kRing * 64;
   MLA_LDS int32_t* tokidx = (MLA_LDS int32_t*)(smem + kMetaOffset);
   MLA_LDS uint32_t* vmask = (MLA_LDS uint32_t*)(tokidx + 8 * kSub);
   MLA_LDS int32_t* wflag = (MLA_LDS int32_t*)(smem + kFlagOffset);
-  MLA_LDS u32x4* pbuf = (MLA_LDS u32x4*)(smem + kPOffset);
+  MLA_LDS float* xrow = (MLA_LDS float*)(smem + kXOffset);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h = lane >> 5;    // lane half (k-group of the MFMA operands)
-  const int l32 = lane & 31;  // query row within the row block
-  const int rb = wave & 1;    // row block
-  const int hf = wave >> 1;   // half of the dims / columns
-  const int partner = wave ^ 2;
+  const int l16 = lane & 15, h4 = lane >> 4;  // 16x16 operand row / k-group
+  const int l32 = lane & 31, h2 = lane >> 5;  // 32x32 operand row / k-group
+  // scores: rows 16 r4 .., tokens 16 tb .. of each sub-tile
+  const int r4 = wave & 3, tb = wave >> 2;
+  const int qrow = 16 * r4 + l16;  // this lane's query row (0..63) in the score and softmax steps
 
   // workgroup -> (worker, row tile); the row tiles of one worker share an XCD
   int w, rt;
@@ -144,45 +148,46 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   constexpr int tok_bytes = FP8 ? kFp8TokenBytes : kBf16TokenBytes;
 
   // ---- per-lane constants -------------------------------------------------------
-  // K operand: token l32, chunk c(kk) = 32 hf + 2 kk + h for kk < 16, and
-  // 64 + 4 hf + 2 (kk - 16) + h for kk = 16, 17.
-  const int ksw = tile_swizzle(l32);
-  int kofs[4], kofs_r[2];
+  // K operand of k-step kk (dims 32 kk ..): token 16 tb + l16, chunk 4 kk + h4,
+  // i.e. kofs[kk & 1] + 128 (kk >> 1) (the swizzle only touches the low 3 bits).
+  int kofs[2];
+  {
+    const int t = 16 * tb + l16;
+    const int sw = tile_swizzle(t);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) kofs[m] = l32 * kBf16TokenBytes + 32 * hf * 16 + (((2 * m + h) ^ ksw) << 4);
-#pragma unroll
-  for (int m = 0; m < 2; ++m) kofs_r[m] = l32 * kBf16TokenBytes + ((64 + ((4 * hf + 2 * m + h) ^ ksw)) << 4);
-  // V^T operand (transposed reads): [s2][e4][parity of the column block]
+    for (int m = 0; m < 2; ++m) kofs[m] = t * kBf16TokenBytes + (((4 * m + h4) ^ sw) << 4);
+  }
+  // V^T operand (transposed reads) of k-step s2, half e4 and the parity of the
+  // 32-column block: the 4 lanes of a quad supply tokens 16 s2 + 8 h2 + 4 e4 + q,
+  // and each lane receives its column at those 4 tokens; columns 64 wave ..
   int vofs[2][2][2];
   {
-    const int tl = 4 * h + ((lane & 15) >> 2);
+    const int q = (lane & 15) >> 2;
     const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int e4 = 0; e4 < 2; ++e4) {
-        const int tok = 16 * s2 + 8 * e4 + tl;
+        const int tok = 16 * s2 + 8 * h2 + 4 * e4 + q;
         const int sw = tile_swizzle(tok);
         const int sb = sw >> 2;
-        const int base = tok * kBf16TokenBytes + 256 * wave + ((cl ^ (sw & 3)) << 4) + 8 * (lane & 1);
+        const int base = tok * kBf16TokenBytes + 128 * wave + ((cl ^ (sw & 3)) << 4) + 8 * (lane & 1);
         vofs[s2][e4][0] = base + 64 * sb;
         vofs[s2][e4][1] = base - 64 * sb;
       }
   }
-  // BF16 staging: load k of this thread fills LDS slot s = (9 wave + k) 64 + lane,
-  // i.e. token dtok[k] of the sub-tile, source chunk dchunk[k]
-  // (byte offset doff[k] = dtok[k] * 1152 + 16 * source chunk within the sub-tile)
-  int dtok[kBf16LoadsPerThread], dchunk[kBf16LoadsPerThread];
-  uint32_t doff[kBf16LoadsPerThread];
-#pragma unroll
-  for (int k = 0; k < kBf16LoadsPerThread; ++k) {
-    const int s = (wave * kBf16LoadsPerThread + k) * 64 + lane;
-    dtok[k] = s / kTokenChunks;
-    dchunk[k] = (s - dtok[k] * kTokenChunks) ^ tile_swizzle(dtok[k]);
-    doff[k] = (uint32_t)(dtok[k] * kBf16TokenBytes + dchunk[k] * 16);
-  }
-  // exchange slots of this lane: [wave][q4][lane]
-  const int xo_base = wave * 4 * 64 + lane, xp_base = partner * 4 * 64 + lane;
+  // P block of this lane (row qrow, tokens 16 tb + 4 h4 + e) in the layout the
+  // PV step reads: [row block qrow / 32][k-step tb][lane 16 (r4 & 1) + l16 + 32 (h4 / 2)]
+  // bf16x8, half h4 & 1.
+  const int pw_off = (((r4 >> 1) * 2 + tb) * 64 + 16 * (r4 & 1) + l16 + 32 * (h4 >> 1)) * 16 + 8 * (h4 & 1);
+  // BF16 staging: load k of this thread fills LDS slot s = 512 k + tid, i.e.
+  // token s / 72 of the sub-tile, stored chunk s % 72 (source chunk: that XOR
+  // the token's swizzle); computed when needed, as registers are scarce.
+  auto slot_token = [&](int k) -> int { return min(k * kDecThreads + tid, kSlots - 1) / kTokenChunks; };
+  auto slot_src = [&](int k, int t) -> int {  // source byte offset of load k within token t's row
+    const int s = min(k * kDecThreads + tid, kSlots - 1);
+    return ((s - t * kTokenChunks) ^ tile_swizzle(t)) * 16;
+  };
 
   for (int stream = bs; stream <= es && stream < p.n_streams; ++stream) {
     const int ntiles = first[stream + 1] - first[stream];
@@ -204,23 +209,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     const int u0 = 2 * lo;
     const int u1 = min(2 * hi, (limit + kSub - 1) / kSub);
 
-    const int row = rt * 64 + rb * kWaveRows + l32;
-    const bool row_ok = row < p.R_stream;
-
-    // Q fragments: dims 256 hf + 16 kk + 8 h (kk < 16), 512 + 32 hf + 16 (kk - 16) + 8 h
+    // Q fragments (B operand of the score MFMA): row qrow, dims 32 kk + 8 h4 ..
     bf16x8 qf[18];
     {
-      const uint16_t* qrow = p.q + (row_base + (row_ok ? row : 0)) * kDQK + 8 * h;
+      const int row = rt * kRowTile + qrow;
+      const bool row_ok = row < p.R_stream;
+      const uint16_t* qr = p.q + (row_base + (row_ok ? row : 0)) * kDQK + 8 * h4;
 #pragma unroll
       for (int kk = 0; kk < 18; ++kk) {
-        const int d = kk < 16 ? 256 * hf + 16 * kk : 512 + 32 * hf + 16 * (kk - 16);
-        u32x4 v = *(const u32x4*)(qrow + d);
+        u32x4 v = *(const u32x4*)(qr + 32 * kk);
         if (!row_ok) v = u32x4{0, 0, 0, 0};
         qf[kk] = __builtin_bit_cast(bf16x8, v);
       }
     }
 
-    f32x16 acc[8];
+    // O^T accumulators: [row block][32-column block], columns 64 wave + 32 ct ..
+    f32x16 acc[2][2];
 
     // ---- per sub-tile metadata ----------------------------------------------------
     // Round u (below) streams sub-tile u + 2 into LDS; whatever it needs to know
@@ -228,12 +232,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     // was fetched rounds ahead into LDS, so no round waits on a load it just issued.
     //
     // BF16 (tiles arrive by direct global->LDS loads): the metadata travels the
-    // same way, into rings of 8 sub-tiles, issued at the start of a round and
-    // landed by its end.  Round u fetches the page of sub-tile u + 3 (dense), or
-    // the indices of sub-tile u + 4 and the pages of sub-tile u + 3's indices
-    // (sparse).  No loaded value ever lands in a register inside the loop: the
-    // compiler could only wait for such a value by draining every direct load
-    // still streaming.
+    // same way, into rings of 8 sub-tiles, issued by wave 0 at the start of a
+    // round and landed by its end.  Round u fetches the page of sub-tile u + 3
+    // (dense), or the indices of sub-tile u + 4 and the pages of sub-tile u + 3's
+    // indices (sparse).  No loaded value ever lands in a register inside the
+    // loop: the compiler could only wait for such a value by draining every
+    // direct load still streaming.
     //
     // FP8 (tiles go through registers): sub-tile u's metadata sits in LDS slot
     // u & 7 (dense: its page; sparse: the token row of each slot, -1 when not
@@ -307,8 +311,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
         return (uint32_t)__ballot(ok);
       }
     };
+    // scores of sub-tile u with the tokens no row attends set to -inf
+    // (this lane: row qrow, tokens 16 tb + 4 h4 + e)
+    auto mask_scores = [&](int u, f32x4& v) {
+      const uint32_t tmask = SPARSE ? sparse_mask(u) : 0u;
+      const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= seqlen;
+      if (!full) {
+        asm volatile("");  // a real branch: full sub-tiles skip the masking
+        const int vcount = seqlen - u * kSub;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tok = 16 * tb + 4 * h4 + e;
+          const bool ok = SPARSE ? ((tmask >> tok) & 1u) != 0 : tok < vcount;
+          v[e] = ok ? v[e] : kNegInf;
+        }
+      }
+    };
     // ---- staging ------------------------------------------------------------------
-    auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((u - u0) % kNBuf) * kSubBytes; };
+    auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((u - u0 + kNBuf) % kNBuf) * kSubBytes; };
     // FP8: byte address of stored token t of sub-tile u (the zero token when not attended)
     auto token_ptr = [&](int u, int t) -> const uint8_t* {
       if (SPARSE) {
@@ -319,107 +339,101 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       const int page = tokidx[(u & 7) * kSub];
       return p.kv + ((int64_t)page * kPage + (u & 1) * kSub + t) * tok_bytes;
     };
-    // BF16 direct loads of sub-tile u: this thread's nine 16-byte pieces.  Dense
-    // tiles use buffer loads against the sub-tile's 36,864 bytes, and tokens past
-    // the sequence end take an out-of-range offset, which loads zeros; sparse
-    // tiles load from per-lane global addresses (the zero token when a slot is
-    // not attended).
-    struct Bf16Loads {
-      __amdgpu_buffer_rsrc_t rs;
-      uint32_t voff[kBf16LoadsPerThread];
-      const uint8_t* src[kBf16LoadsPerThread];
-    };
-    auto stage_prep = [&](int u, Bf16Loads& L) {
+    // BF16 direct loads of sub-tile u: this thread's five (or four) 16-byte
+    // pieces, each issued as soon as its address is known (no address arrays:
+    // registers are scarce).  Dense tiles use buffer loads against the
+    // sub-tile's 36,864 bytes, and tokens past the sequence end take an
+    // out-of-range offset, which loads zeros; sparse tiles load from per-lane
+    // global addresses (the zero token when a slot is not attended).
+    auto stage_bf16 = [&](int u, MLA_LDS char* buf) {
       const int r = (u & (kRing - 1)) * 64;
+      auto dst = [&](int k) { return (MLA_LDS void*)(buf + k * (kDecThreads * 16) + wave * 1024); };
       if constexpr (SPARSE) {
         // token row of slot l32, then of each load's token
         const int idx = ring_idx[r + l32];
         const int pg = ring_pg[r + l32];
         const int tok = (slot_ok(u) && idx >= 0) ? pg * kPage + (idx & 63) : -1;
 #pragma unroll
-        for (int k = 0; k < kBf16LoadsPerThread; ++k) {
-          const int tk = __shfl(tok, dtok[k]);
-          L.src[k] = (tk >= 0 ? p.kv + (int64_t)tk * kBf16TokenBytes : g_zero_token) + dchunk[k] * 16;
+        for (int k = 0; k < kLoads; ++k) {
+          if (k == kLoads - 1 && wave >= 4) break;
+          const int t = slot_token(k);
+          const int tk = __shfl(tok, t);
+          const uint8_t* src = (tk >= 0 ? p.kv + (int64_t)tk * kBf16TokenBytes : g_zero_token) + slot_src(k, t);
+          global_load_lds16((const void*)src, dst(k));
         }
       } else {
         const int page = __builtin_amdgcn_readfirstlane(ring_pg[r]);
         const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
-        L.rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, kSubBytes, kBufferFlags);
-        if ((u + 1) * kSub <= seqlen) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, kSubBytes, kBufferFlags);
+        const int valid = seqlen - u * kSub;  // tokens of the sub-tile inside the sequence
 #pragma unroll
-          for (int k = 0; k < kBf16LoadsPerThread; ++k) L.voff[k] = doff[k];
-        } else {
-          asm volatile("");  // a real branch: only the last sub-tile pays for this
-          const int valid = seqlen - u * kSub;  // tokens of the sub-tile inside the sequence
-#pragma unroll
-          for (int k = 0; k < kBf16LoadsPerThread; ++k) L.voff[k] = dtok[k] < valid ? doff[k] : (uint32_t)kSubBytes;
+        for (int k = 0; k < kLoads; ++k) {
+          if (k == kLoads - 1 && wave >= 4) break;
+          const int t = slot_token(k);
+          buffer_load_lds16(rs, dst(k), t < valid ? (uint32_t)(t * kBf16TokenBytes + slot_src(k, t)) : (uint32_t)kSubBytes);
         }
       }
     };
-    auto stage_issue = [&](const Bf16Loads& L, int k, MLA_LDS char* buf) {
-      MLA_LDS void* dst = (MLA_LDS void*)(buf + (wave * kBf16LoadsPerThread + k) * 1024);
-      if constexpr (SPARSE)
-        __builtin_amdgcn_global_load_lds((const void*)L.src[k], dst, 16, 0, 0);
-      else
-        buffer_load_lds16(L.rs, dst, L.voff[k]);
-    };
-    auto stage_bf16 = [&](int u, MLA_LDS char* buf) {
-      Bf16Loads L;
-      stage_prep(u, L);
-#pragma unroll
-      for (int k = 0; k < kBf16LoadsPerThread; ++k) stage_issue(L, k, buf);
-    };
     auto load_fp8 = [&](int u, RawFp8& r) {
-      const int t = tid >> 3, j = tid & 7;
+      const int t = tid >> 4, j = tid & 15;
       const uint8_t* pt = token_ptr(u, t);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r.v[i] = *(const u32x4*)(pt + 16 * (j + 8 * i));
+      for (int i = 0; i < 2; ++i) r.v[i] = *(const u32x4*)(pt + 16 * (j + 16 * i));
       r.sc = *(const u32x4*)(pt + kFp8Dims);
-      r.r = *(const u32x4*)(pt + kFp8Dims + 16 + 16 * j);
+      r.r = *(const u32x4*)(pt + kFp8Dims + 16 + 16 * (j & 7));
     };
     auto store_fp8 = [&](const RawFp8& r, MLA_LDS char* buf) {
-      const int t = tid >> 3, j = tid & 7;
+      const int t = tid >> 4, j = tid & 15;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = j + 8 * i;
+      for (int i = 0; i < 2; ++i) {
+        const int c = j + 16 * i;
         u32x4 lo, hi;
-        dequant16(r.v[i], pick_scale(r.sc, i), lo, hi);
+        dequant16(r.v[i], pick_scale(r.sc, c >> 3), lo, hi);
         *(MLA_LDS u32x4*)(buf + tile_slot(t, 2 * c) * 16) = lo;
         *(MLA_LDS u32x4*)(buf + tile_slot(t, 2 * c + 1) * 16) = hi;
       }
-      *(MLA_LDS u32x4*)(buf + tile_slot(t, 64 + j) * 16) = r.r;
+      if (j < 8) *(MLA_LDS u32x4*)(buf + tile_slot(t, 64 + j) * 16) = r.r;
     };
-    // ---- score exchange and PV pieces ---------------------------------------------
-    // The pair adds its two partial S^T blocks through LDS: slots [wave][q4][lane].
-    MLA_LDS f32x4* xo = xbuf + xo_base;
-    MLA_LDS f32x4* xp = xbuf + xp_base;
+    // ---- operand reads ------------------------------------------------------------
     auto kread = [&](MLA_LDS char* kb, int kk) -> bf16x8 {
-      const int off = kk < 16 ? kofs[kk & 3] + (kk >> 2) * 128 : kofs_r[kk - 16];
-      return *(MLA_LDS bf16x8*)(kb + off);
+      return *(MLA_LDS bf16x8*)(kb + kofs[kk & 1] + (kk >> 1) * 128);
     };
-    // V^T fragment (this wave's 32-column block cb of its 128 columns, 16-token k-step s2)
-    auto vread = [&](MLA_LDS char* vb, int s2, int cb) -> bf16x8 {
-      const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(vb + vofs[s2][0][cb & 1] + 64 * cb));
-      const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(vb + vofs[s2][1][cb & 1] + 64 * cb));
+    // V^T fragment: 32-column block ct of this wave's 64 columns, 16-token k-step s2
+    auto vread = [&](MLA_LDS char* vb, int s2, int ct) -> bf16x8 {
+      const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(vb + vofs[s2][0][ct & 1] + 64 * ct));
+      const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(vb + vofs[s2][1][ct & 1] + 64 * ct));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    // P fragment (B operand of PV): row block rb, k-step s2 of the sub-tile of parity par
+    auto pread = [&](int par, int rb, int s2) -> bf16x8 {
+      return *(MLA_LDS bf16x8*)(pbuf + par * kPHalf + ((rb * 2 + s2) * 64 + lane) * 16);
+    };
+    // row maximum over the lanes (h4 = 0..3) holding this lane's row
+    auto row_max16 = [&](float v) -> float {
+      v = fmaxf(v, __shfl_xor(v, 16));
+      return fmaxf(v, __shfl_xor(v, 32));
+    };
 
-    // Reference maximum m_ref (log2 domain, per row): the row's first finite
-    // sub-tile maximum + kRefLift, fixed for the whole split, so P = 2^(x - m_ref)
-    // stays within [2^-126, 2^(kRefLift + kRefRoom)] for every score within
-    // (kRefRoom, 126 - kRefLift) of that first maximum, and O changes only through
-    // MFMAs.  A score more than kRefRoom above m_ref (scores spread by over ~60
-    // natural-log units) marks the pass as overflowed and the split is recomputed
-    // from the start with the split's true maximum as the reference.
+    // Reference maximum m_ref (log2 domain, per row): the row's maximum over the
+    // split's first sub-tile + kRefLift, fixed for the whole split, so
+    // P = 2^(x - m_ref) stays within [2^-126, 2^(kRefLift + kRefRoom)] for every
+    // score within (kRefRoom, 126 - kRefLift) of that maximum, and O changes only
+    // through MFMAs.  A score more than kRefRoom above m_ref (scores spread by
+    // over ~60 natural-log units), or a finite score in a row whose first
+    // sub-tile was fully masked, marks the pass as overflowed and the split is
+    // recomputed from the start with the split's true row maximum as the
+    // reference.
     float m_ref = kNegInf, m_seen = kNegInf, l_sum = 0.f;
     bool redo = false;
+    int pass = 0;  // at most two: the second pass runs with the split's row maximum
     do {
       l_sum = 0.f;
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[cb][e] = 0.f;
-      if (redo) m_ref = m_seen + kRefLift;
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[rb][ct][e] = 0.f;
       bool overflow = false;
 
       // ---- prologue: metadata, sub-tiles u0 and u0 + 1 in LDS, S of u0 ------------
@@ -447,30 +461,32 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
         stage_bf16(u0 + 1, buffer(u0 + 1));
         tile_barrier_drain();
       }
-      float x[16];  // full scores S^T of the sub-tile whose softmax comes next
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};  // S^T of the sub-tile whose softmax comes next
       {
         MLA_LDS char* kb = buffer(u0);
-        f32x16 s = {};
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kb, kk), qf[kk], s, 0, 0, 0);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) xo[q4 * 64] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-        lds_barrier();
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 o = xp[q4 * 64];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * q4 + e] = hf == 0 ? s[4 * q4 + e] + o[e] : o[e] + s[4 * q4 + e];
-        }
+        for (int kk = 0; kk < 18; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kread(kb, kk), qf[kk], s, 0, 0, 0);
+      }
+      if (!redo) {
+        // the reference of each row from sub-tile u0 (both token blocks of the row)
+        f32x4 v = s;
+        mask_scores(u0, v);
+        float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        mx = row_max16(mx);
+        if (h4 == 0) xrow[tb * 64 + qrow] = mx;
+        __syncthreads();
+        const float m0 = fmaxf(xrow[qrow], xrow[64 + qrow]) * p.scale_log2;
+        m_ref = m0 == kNegInf ? kNegInf : m0 + kRefLift;
+        __syncthreads();
       }
 
-      // One round u: PV of sub-tile u (buffer vb) and QK of sub-tile u + 1 (kb),
-      // whose MFMAs run under u's softmax, while sub-tile u + 2 streams into nxt.
-      // The buffers are distinct, and saying so (restrict) lets the compiler keep
-      // the direct loads in flight across the reads of vb and kb.
+      // One round u: softmax of sub-tile u (its P to LDS), PV of sub-tile u - 1
+      // (V^T from vb), QK of sub-tile u + 1 (K from kb), while sub-tile u + 2
+      // streams into nxt.  The buffers are distinct, and saying so (restrict) lets
+      // the compiler keep the direct loads in flight across the reads of vb and kb.
       auto round = [&](const int u, MLA_LDS char* __restrict__ vb, MLA_LDS char* __restrict__ kb,
                        MLA_LDS char* __restrict__ nxt) __attribute__((always_inline)) {
-        // ---- phase A: metadata, streaming, QK(u + 1) under softmax(u) ---------------
+        const bool pv = u > u0;  // workgroup-uniform
         int meta = 0;  // FP8: metadata of sub-tile u + 4 (published at the end of this round)
         if constexpr (FP8) {
           if (SPARSE) {
@@ -480,180 +496,174 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
             meta = page_load(u + 4);
           }
         } else {
-          meta_dma(u);
+          if (wave == 0) meta_dma(u);
         }
         __builtin_amdgcn_sched_barrier(0);  // metadata loads stay ahead of the tile loads
-        Bf16Loads L;
+        // sub-tile u + 2: direct loads (BF16) or the registers loaded last round (FP8)
         if constexpr (FP8) {
-          store_fp8(raw, nxt);  // sub-tile u + 2 arrived during the last round
+          store_fp8(raw, nxt);
           load_fp8(u + 3, raw);
         } else {
-          stage_prep(u + 2, L);
+          stage_bf16(u + 2, nxt);
         }
-        // mask of sub-tile u: lane holds row l32, tokens 8 (e / 4) + 4 h + e % 4
-        const uint32_t tmask = SPARSE ? sparse_mask(u) : 0u;
-        const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= seqlen;
-        if (!full) {
-          asm volatile("");  // a real branch: full sub-tiles skip the masking
-          const int vcount = seqlen - u * kSub;
+        __builtin_amdgcn_sched_barrier(0);
+        // softmax of sub-tile u: P = 2^(scale_log2 S - m_ref)
+        {
+          f32x4 v = s;
+          mask_scores(u, v);
+          const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])) * p.scale_log2;
+          m_seen = fmaxf(m_seen, mx);
+          overflow |= (m_ref == kNegInf && mx != kNegInf) || mx > m_ref + kRefRoom;
+          const float msafe = m_ref == kNegInf ? 0.f : m_ref;
+          bf16x2 p01, p23;
+          float pe[4];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int tok = 8 * (e >> 2) + 4 * h + (e & 3);
-            const bool ok = SPARSE ? ((tmask >> tok) & 1u) != 0 : tok < vcount;
-            x[e] = ok ? x[e] : kNegInf;
-          }
+          for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[e], p.scale_log2, -msafe));
+          l_sum += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+          p01.x = (__bf16)pe[0];
+          p01.y = (__bf16)pe[1];
+          p23.x = (__bf16)pe[2];
+          p23.y = (__bf16)pe[3];
+          *(MLA_LDS u32x2*)(pbuf + (u & 1) * kPHalf + pw_off) =
+              u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
         }
-        // The issue order is pinned (a scheduling barrier per step): MFMA kk of
-        // QK(u + 1), the K fragment six steps ahead, one of the nine tile loads,
-        // then a slice of u's softmax.  Softmax: row maximum (log2 domain, the
-        // scale is positive), reference update, then P = 2^(scale_log2 S - m_ref)
-        // for this wave's k-step (the pair splits the exponentials: the hf wave
-        // takes tokens 16 hf .. 16 hf + 15, its x[8 hf ..]).
-        constexpr int kAhead = 6;
+        // PV(u - 1): O^T += V^T P^T, P of every wave, V^T of this wave's columns
+        if (pv) {
+          bf16x8 pp[2][2], va[2][2];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) pp[rb][s2] = pread((u - 1) & 1, rb, s2);
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) va[s2][ct] = vread(vb, s2, ct);
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct)
+                acc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s2][ct], pp[rb][s2], acc[rb][ct], 0, 0, 0);
+        }
+        // QK(u + 1), K fragments read kAhead steps ahead
+        constexpr int kAhead = 4;
         bf16x8 kf[18];
 #pragma unroll
         for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kb, kk);
         __builtin_amdgcn_sched_barrier(0);
-        f32x16 s = {};
-        float m4[4], mx = 0.f, msafe = 0.f;
-        float xs[8];
-        bf16x8 pown;
+        s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 18; ++kk) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], s, 0, 0, 0);
           if (kk + kAhead < 18) kf[kk + kAhead] = kread(kb, kk + kAhead);
-          if constexpr (!FP8) {
-            if (kk < kBf16LoadsPerThread) stage_issue(L, kk, nxt);
-          }
-          if (kk < 4) {
-            m4[kk] = fmaxf(fmaxf(x[4 * kk], x[4 * kk + 1]), fmaxf(x[4 * kk + 2], x[4 * kk + 3]));
-          } else if (kk == 4) {
-            mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-            // lanes l and l ^ 32 hold the same row (a VALU lane swap, no LDS)
-            mx = halves_max(mx) * p.scale_log2;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xs[e] = hf == 0 ? x[e] : x[8 + e];
-          } else if (kk == 5) {
-            m_seen = fmaxf(m_seen, mx);
-            if (m_ref == kNegInf && mx != kNegInf) m_ref = mx + kRefLift;
-            overflow |= mx > m_ref + kRefRoom;
-            msafe = m_ref == kNegInf ? 0.f : m_ref;
-          } else if (kk < 14) {
-            const int e = kk - 6;
-            const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[e], p.scale_log2, -msafe));
-            l_sum += pe;
-            pown[e] = (__bf16)pe;
-          } else if (kk == 14) {
-            pbuf[(rb * 2 + hf) * 64 + lane] = __builtin_bit_cast(u32x4, pown);
-          }
           __builtin_amdgcn_sched_barrier(0);
         }
-        lds_barrier();  // every P block of sub-tile u is in LDS
-
-        // ---- phase B: O^T += V^T P^T for sub-tile u ----------------------------------
-        const bf16x8 pb0 = __builtin_bit_cast(bf16x8, pbuf[(rb * 2 + 0) * 64 + lane]);
-        const bf16x8 pb1 = __builtin_bit_cast(bf16x8, pbuf[(rb * 2 + 1) * 64 + lane]);
-        const bf16x8 qb0 = __builtin_bit_cast(bf16x8, pbuf[((rb ^ 1) * 2 + 0) * 64 + lane]);
-        const bf16x8 qb1 = __builtin_bit_cast(bf16x8, pbuf[((rb ^ 1) * 2 + 1) * 64 + lane]);
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 va[2][4];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) va[s2][cb] = vread(vb, s2, cb);
-        __builtin_amdgcn_sched_barrier(0);
-        // acc[0..3]: rows of this wave's row block, acc[4..7]: the other row block;
-        // columns 128 wave + 32 cb
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s2][cb], s2 ? pb1 : pb0, acc[cb], 0, 0, 0);
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            acc[4 + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s2][cb], s2 ? qb1 : qb0, acc[4 + cb], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // the PV MFMAs issue before the round's last waits
-        // partial S^T of sub-tile u + 1 to the partner
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) xo[q4 * 64] = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
         if constexpr (FP8) {
           if (wave == 0) publish(u + 4, meta);
           lds_barrier();  // sub-tile u + 2 went through registers
         } else {
           tile_barrier_drain();  // sub-tile u + 2 and the metadata have landed
         }
-        // ---- phase C: S of sub-tile u + 1 = (hf 0 partial) + (hf 1 partial) ----------
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 o = xp[q4 * 64];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * q4 + e] = hf == 0 ? s[4 * q4 + e] + o[e] : o[e] + s[4 * q4 + e];
-        }
       };
-      for (int u = u0; u < u1; ++u) round(u, buffer(u), buffer(u + 1), buffer(u + 2));
-      // the last round streamed sub-tiles past the end: let them land before LDS is reused
-      tile_barrier_drain();
+      for (int u = u0; u < u1; ++u) round(u, buffer(u - 1), buffer(u + 1), buffer(u + 2));
+
+      // PV of the last sub-tile
+      {
+        const int u = u1;
+        MLA_LDS char* vb = buffer(u - 1);
+        bf16x8 pp[2][2], va[2][2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) pp[rb][s2] = pread((u - 1) & 1, rb, s2);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) va[s2][ct] = vread(vb, s2, ct);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+              acc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s2][ct], pp[rb][s2], acc[rb][ct], 0, 0, 0);
+      }
 
       // the restart must be taken by the whole workgroup (it contains barriers);
       // the vote is over every lane, so it is taken before the lane-0 store
       const bool wave_overflow = __ballot(overflow) != 0;
       if (lane == 0) wflag[wave] = wave_overflow ? 1 : 0;
       __syncthreads();
-      redo = (wflag[0] | wflag[1] | wflag[2] | wflag[3]) != 0;
+      redo = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) redo |= wflag[i] != 0;
+      redo = redo && pass == 0;
+      ++pass;
+      if (redo) {
+        // the split's row maximum over every lane and token block holding the row
+        const float ms = row_max16(m_seen);
+        if (h4 == 0) xrow[tb * 64 + qrow] = ms;
+        __syncthreads();
+        const float m0 = fmaxf(xrow[qrow], xrow[64 + qrow]);
+        m_ref = m0 == kNegInf ? kNegInf : m0 + kRefLift;
+      }
       __syncthreads();
     } while (redo);
 
     // ---- epilogue -------------------------------------------------------------------
-    // This wave holds O^T for both row blocks (columns 128 wave ..); each row's
-    // l and reference come from the pair that owns the row.
+    // l of each row: this lane's sum over its tokens, over the 4 lanes of the row
+    // and the two token blocks; m_ref of each row from its score waves.
+    l_sum += __shfl_xor(l_sum, 16);
     l_sum += __shfl_xor(l_sum, 32);
+    if (h4 == 0) {
+      xrow[tb * 64 + qrow] = l_sum;
+      if (tb == 0) xrow[128 + qrow] = m_ref;
+    }
+    __syncthreads();
     {
-      // l[row block][k-step][32] (each wave summed its k-step), then m_ref[64]
-      MLA_LDS float* lm = (MLA_LDS float*)(smem + kXOffset);
-      if (h == 0) {
-        lm[(rb * 2 + hf) * 32 + l32] = l_sum;
-        if (hf == 0) lm[128 + rb * 32 + l32] = m_ref;
-      }
-      __syncthreads();
-      const float l_own = lm[(rb * 2) * 32 + l32] + lm[(rb * 2 + 1) * 32 + l32];
-      const float l_oth = lm[((rb ^ 1) * 2) * 32 + l32] + lm[((rb ^ 1) * 2 + 1) * 32 + l32];
-      const float m_oth = lm[128 + (rb ^ 1) * 32 + l32];
+      // this lane's first output column; computed here (not hoisted out of the
+      // stream loop, where it would hold registers the main loop needs)
+      int col = 64 * wave + 4 * h2;
+      int lrow = l32;
+      asm volatile("" : "+v"(col), "+v"(lrow));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float lj = j == 0 ? l_own : l_oth, mj = j == 0 ? m_ref : m_oth;
-        const int rowj = rt * 64 + (rb ^ j) * kWaveRows + l32;
+      for (int rb = 0; rb < 2; ++rb) {
+        const int rho = 32 * rb + lrow;  // row within the tile
+        const float lj = xrow[rho] + xrow[64 + rho];
+        const float mj = xrow[128 + rho];
+        const int rowj = rt * kRowTile + rho;
         const bool empty = !(lj > 0.f);
         const float inv = empty ? 0.f : 1.f / lj;
         const float lse_v = empty ? kNegInf : (mj + __log2f(lj)) * 0.69314718055994531f;
         if (rowj < p.R_stream) {
           if (final_out) {
-            uint16_t* orow = p.o + (row_base + rowj) * kDV + 128 * wave + 4 * h;
+            uint16_t* orow = p.o + (row_base + rowj) * kDV + col;
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const f32x16& a = acc[4 * j + cb];
+                const f32x16& a = acc[rb][ct];
                 bf16x2 v0, v1;
                 v0.x = (__bf16)(a[4 * i + 0] * inv);
                 v0.y = (__bf16)(a[4 * i + 1] * inv);
                 v1.x = (__bf16)(a[4 * i + 2] * inv);
                 v1.y = (__bf16)(a[4 * i + 3] * inv);
-                *(u32x2*)(orow + cb * 32 + 8 * i) =
+                *(u32x2*)(orow + ct * 32 + 8 * i) =
                     u32x2{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1)};
               }
-            if (j == 0 && h == 0 && hf == 0) p.lse[row_base + rowj] = lse_v;
+            if (wave == 0 && h2 == 0) p.lse[row_base + rowj] = lse_v;
           } else {
-            float* prow = p.part_o + ((int64_t)sid * p.R_stream + rowj) * kDV + 128 * wave + 4 * h;
+            float* prow = p.part_o + ((int64_t)sid * p.R_stream + rowj) * kDV + col;
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const f32x16& a = acc[4 * j + cb];
-                *(f32x4*)(prow + cb * 32 + 8 * i) =
+                const f32x16& a = acc[rb][ct];
+                *(f32x4*)(prow + ct * 32 + 8 * i) =
                     f32x4{a[4 * i] * inv, a[4 * i + 1] * inv, a[4 * i + 2] * inv, a[4 * i + 3] * inv};
               }
-            if (j == 0 && h == 0 && hf == 0) p.part_lse[(int64_t)sid * p.R_stream + rowj] = lse_v;
+            if (wave == 0 && h2 == 0) p.part_lse[(int64_t)sid * p.R_stream + rowj] = lse_v;
           }
         }
       }
@@ -671,7 +681,7 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(p.W * p.n_rt), dim3(kThreads), kLdsBytes, stream, p);
+  hipLaunchKernelGGL(kern, dim3(p.W * p.n_rt), dim3(kDecThreads), kLdsBytes, stream, p);
   return hipGetLastError();
 }
 
