@@ -95,12 +95,14 @@ static_assert(kSlots == 4 * kDecThreads + kDecThreads / 2, "staging split");
 // Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle.
 constexpr int kBufferFlags = 0x00020000;
 
-// FP8 registers of one sub-tile for this thread: token tid / 16, code chunks
-// j and j + 16 (j = tid % 16; chunk c uses scale c / 8), the four scales and
-// RoPE chunk j % 8 (stored by j < 8).
+// FP8 registers of one sub-tile for this thread: for k = 0..3 the 8 codes of
+// dims 8 lane .. of token 8 k + wave and their scale (scale lane / 16), and for
+// waves 0..3 the RoPE chunk tid % 8 (dims 512 + 8 (tid % 8) ..) of token tid / 8.
+// A wave thus dequantises 64 consecutive 16-byte chunks of one token per store
+// (conflict-free LDS writes) from 512 consecutive code bytes.
 struct RawFp8 {
-  u32x4 v[2];
-  u32x4 sc;
+  u32x2 v[4];
+  float sc[4];
   u32x4 r;
 };
 
@@ -375,24 +377,21 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       }
     };
     auto load_fp8 = [&](int u, RawFp8& r) {
-      const int t = tid >> 4, j = tid & 15;
-      const uint8_t* pt = token_ptr(u, t);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) r.v[i] = *(const u32x4*)(pt + 16 * (j + 16 * i));
-      r.sc = *(const u32x4*)(pt + kFp8Dims);
-      r.r = *(const u32x4*)(pt + kFp8Dims + 16 + 16 * (j & 7));
+      for (int k = 0; k < 4; ++k) {
+        const uint8_t* pt = token_ptr(u, 8 * k + wave);
+        r.v[k] = *(const u32x2*)(pt + 8 * lane);
+        r.sc[k] = *(const float*)(pt + kFp8Dims + 4 * (lane >> 4));
+      }
+      if (wave < 4) r.r = *(const u32x4*)(token_ptr(u, tid >> 3) + kFp8Dims + 16 + 16 * (tid & 7));
     };
     auto store_fp8 = [&](const RawFp8& r, MLA_LDS char* buf) {
-      const int t = tid >> 4, j = tid & 15;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = j + 16 * i;
-        u32x4 lo, hi;
-        dequant16(r.v[i], pick_scale(r.sc, c >> 3), lo, hi);
-        *(MLA_LDS u32x4*)(buf + tile_slot(t, 2 * c) * 16) = lo;
-        *(MLA_LDS u32x4*)(buf + tile_slot(t, 2 * c + 1) * 16) = hi;
+      for (int k = 0; k < 4; ++k) {
+        const u32x2 a = dequant4(r.v[k].x, r.sc[k]), b = dequant4(r.v[k].y, r.sc[k]);
+        *(MLA_LDS u32x4*)(buf + tile_slot(8 * k + wave, lane) * 16) = u32x4{a.x, a.y, b.x, b.y};
       }
-      if (j < 8) *(MLA_LDS u32x4*)(buf + tile_slot(t, 64 + j) * 16) = r.r;
+      if (wave < 4) *(MLA_LDS u32x4*)(buf + tile_slot(tid >> 3, 64 + (tid & 7)) * 16) = r.r;
     };
     // ---- operand reads ------------------------------------------------------------
     auto kread = [&](MLA_LDS char* kb, int kk) -> bf16x8 {
