@@ -55,7 +55,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_lse_combine.argtypes = [ctypes.c_int64, P, P, P, P]
         L.oracle_mla_decode.restype = None
         L.oracle_mla_decode.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int, P,
-                                        P, ctypes.c_int, ctypes.c_double, P, ctypes.c_int64, P, P]
+                                        P, ctypes.c_int, ctypes.c_int, ctypes.c_double, P, ctypes.c_int64, P, P]
         L.oracle_fp8_dequant_bf16.restype = ctypes.c_uint16
         L.oracle_fp8_dequant_bf16.argtypes = [ctypes.c_uint8, ctypes.c_float]
         L.oracle_schedule.restype = ctypes.c_int
@@ -118,13 +118,14 @@ def lse_combine(o_parts, lse_parts) -> Tuple[np.ndarray, float]:
 
 
 def mla_decode(q_bits, kvcache_bytes, is_fp8: bool, block_table, cache_seqlens, indices, scale: float,
-               rows=None) -> Tuple[np.ndarray, np.ndarray]:
+               rows=None, causal: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """o [n_rows, 512] and lse [n_rows] in float64 for the listed flat rows
     (b * s_q + s) * h_q + h, or all rows when rows is None.
 
     q_bits: uint16/int16 [B, s_q, h_q, 576]; kvcache_bytes: uint8 view of the
     cache; block_table int32 [B, max_blocks]; cache_seqlens int32 [B];
-    indices int32 [B, s_q, topk] or None.
+    indices int32 [B, s_q, topk] or None.  causal: dense only; query token s
+    sees positions j <= seqlen_b - s_q + s.
     """
     q = _c(q_bits, np.uint16)
     if q.ndim != 4 or q.shape[3] != D_QK:
@@ -135,6 +136,8 @@ def mla_decode(q_bits, kvcache_bytes, is_fp8: bool, block_table, cache_seqlens, 
     sl = _c(cache_seqlens, np.int32)
     idx = None if indices is None else _c(indices, np.int32)
     topk = 0 if idx is None else int(idx.shape[2])
+    if causal and idx is not None:
+        raise ValueError("causal masking is defined for dense decoding only")
     if rows is None:
         r = None
         n = B * s_q * h_q
@@ -144,11 +147,11 @@ def mla_decode(q_bits, kvcache_bytes, is_fp8: bool, block_table, cache_seqlens, 
     o = np.zeros((n, D_V), dtype=np.float64)
     lse = np.zeros(n, dtype=np.float64)
     lib().oracle_mla_decode(_ptr(q), B, s_q, h_q, _ptr(kv), int(is_fp8), _ptr(bt), int(bt.shape[1]), _ptr(sl), _ptr(idx),
-                            topk, float(scale), _ptr(r), n, _ptr(o), _ptr(lse))
+                            topk, int(bool(causal)), float(scale), _ptr(r), n, _ptr(o), _ptr(lse))
     return o, lse
 
 
-def problem_decode(prob, rows=None) -> Tuple[np.ndarray, np.ndarray]:
+def problem_decode(prob, rows=None, causal: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """mla_decode on an mla_inputs.Problem (CPU torch tensors)."""
     import torch
 
@@ -156,7 +159,7 @@ def problem_decode(prob, rows=None) -> Tuple[np.ndarray, np.ndarray]:
     kv = prob.kvcache.contiguous().view(torch.uint8).numpy()
     idx = None if prob.indices is None else prob.indices.numpy()
     return mla_decode(q, kv, prob.is_fp8, prob.block_table.numpy(), prob.cache_seqlens.numpy(), idx,
-                      prob.softmax_scale, rows)
+                      prob.softmax_scale, rows, causal)
 
 
 def fp8_dequant_bf16(codes, scales) -> np.ndarray:

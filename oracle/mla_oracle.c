@@ -41,8 +41,15 @@
  *   - lse is the natural log-sum-exp of the scaled scores;
  *   - an empty attended set gives o = 0 and lse = -inf;
  *   - duplicate indices count with multiplicity;
- *   - decode is non-causal: every query token of a request sees all seqlen_b
- *     tokens (dense) or its own index list (sparse);
+ *   - decode is non-causal by default: every query token of a request sees all
+ *     seqlen_b tokens (dense) or its own index list (sparse);
+ *   - with the causal flag (the usage example passes causal=True for
+ *     autoregressive decoding; geoz.com.cn, usage example section) the dense
+ *     mask is aligned to the end of the cache: the s_q query tokens are the
+ *     last s_q positions, so query token s sees positions
+ *     j <= seqlen_b - s_q + s (an empty set when that is negative); the flag is
+ *     not defined for sparse decoding, whose index lists already decide what
+ *     each query token sees;
  *   - sparse indices are logical token positions translated through
  *     block_table;
  *   - FP8 byte layout: byte d (d < 512) holds dim d as OCP e4m3fn; bytes
@@ -232,14 +239,21 @@ void oracle_lse_combine(int64_t n_parts, const double* o_parts, const double* ls
 
 /*
  * The attended positions of query row (b, s): all of [0, seqlen_b) when
- * indices is NULL, else the non-(-1) entries of indices[b, s, :topk].
+ * indices is NULL (with causal != 0, only [0, seqlen_b - s_q + s + 1)), else the
+ * non-(-1) entries of indices[b, s, :topk].
  * Returns the count; pos must hold max(seqlen_b, topk) entries.
  */
 int64_t oracle_attended_positions(const int32_t* cache_seqlens, const int32_t* indices, int s_q, int topk, int b, int s,
-                                  int64_t* pos) {
+                                  int causal, int64_t* pos) {
   int64_t n = 0, j;
   if (indices == NULL) {
-    for (j = 0; j < cache_seqlens[b]; ++j) pos[n++] = j;
+    int64_t end = cache_seqlens[b];
+    if (causal) {
+      int64_t last = (int64_t)cache_seqlens[b] - s_q + s; /* the query token's own position */
+      if (last + 1 < end) end = last + 1;
+      if (end < 0) end = 0;
+    }
+    for (j = 0; j < end; ++j) pos[n++] = j;
     return n;
   }
   for (j = 0; j < topk; ++j) {
@@ -257,7 +271,8 @@ int64_t oracle_attended_positions(const int32_t* cache_seqlens, const int32_t* i
  */
 void oracle_mla_decode(const uint16_t* q, int B, int s_q, int h_q, const uint8_t* kvcache, int is_fp8,
                        const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, const int32_t* indices,
-                       int topk, double scale, const int64_t* rows, int64_t n_rows, double* o, double* lse) {
+                       int topk, int causal, double scale, const int64_t* rows, int64_t n_rows, double* o,
+                       double* lse) {
   int64_t r;
   int64_t cap = topk;
   int b;
@@ -270,7 +285,7 @@ void oracle_mla_decode(const uint16_t* q, int B, int s_q, int h_q, const uint8_t
     int s = (int)((row / h_q) % s_q);
     int bb = (int)(row / ((int64_t)h_q * s_q));
     int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(cap > 0 ? cap : 1));
-    int64_t n = oracle_attended_positions(cache_seqlens, indices, s_q, topk, bb, s, pos);
+    int64_t n = oracle_attended_positions(cache_seqlens, indices, s_q, topk, bb, s, causal, pos);
     oracle_attend(q + row * ORACLE_D_QK, kvcache, is_fp8, block_table + (int64_t)bb * max_blocks, pos, n, scale,
                   o + r * ORACLE_D_V, lse + r);
     free(pos);

@@ -39,8 +39,12 @@ def library_latents(prob):
     return prob.kvcache.reshape(-1, mi.D_QK).to(torch.float64)
 
 
-def library_attention(prob):
-    """o [B, s_q, h_q, 512], lse [B, s_q, h_q] via torch SDPA / logsumexp in float64 (non-empty rows)."""
+def library_attention(prob, causal=False):
+    """o [B, s_q, h_q, 512], lse [B, s_q, h_q] via torch SDPA / logsumexp in float64 (non-empty rows).
+
+    causal (dense): a boolean SDPA mask over the whole sequence, allowing
+    position j for query token s when j <= seqlen - s_q + s; rows with no
+    allowed position stay NaN."""
     K_all = library_latents(prob)
     B, s_q, h_q = prob.B, prob.s_q, prob.h_q
     o = torch.full((B, s_q, h_q, 512), float("nan"), dtype=torch.float64)
@@ -54,18 +58,25 @@ def library_attention(prob):
                 pos = pos[pos != -1]
             if pos.numel() == 0:
                 continue
+            allowed = torch.ones(pos.numel(), dtype=torch.bool)
+            if causal:
+                allowed = pos <= int(prob.cache_seqlens[b]) - s_q + s
+                if not bool(allowed.any()):
+                    continue
             phys = prob.block_table[b].to(torch.int64)[pos // 64] * 64 + pos % 64
             K = K_all[phys]
             q = prob.q[b, s].to(torch.float64)
+            mask = allowed[None, None, None, :].expand(1, 1, h_q, pos.numel())
             out = F.scaled_dot_product_attention(q[None, None], K[None, None], K[None, None, :, :512].contiguous(),
-                                                 scale=prob.softmax_scale)
+                                                 attn_mask=mask, scale=prob.softmax_scale)
             o[b, s] = out[0, 0]
-            lse[b, s] = torch.logsumexp(prob.softmax_scale * (q @ K.T), dim=-1)
+            sc = prob.softmax_scale * (q @ K.T)
+            lse[b, s] = torch.logsumexp(sc.masked_fill(~allowed[None, :], float("-inf")), dim=-1)
     return o, lse
 
 
-def run_oracle(prob, rows=None):
-    o, lse = oracle.problem_decode(prob, rows)
+def run_oracle(prob, rows=None, causal=False):
+    o, lse = oracle.problem_decode(prob, rows, causal)
     if rows is None:
         o = o.reshape(prob.B, prob.s_q, prob.h_q, 512)
         lse = lse.reshape(prob.B, prob.s_q, prob.h_q)
@@ -407,3 +418,57 @@ def test_schedule_covers_every_tile_once(seed):
     _walk(sched, off, tiles, q, W)
     busy = sum(1 for w in range(W) if not (sched[w, 0] == sched[w, 2] and sched[w, 1] == sched[w, 3]))
     assert busy == min(W, -(-N // q)) if N else busy == 0
+
+
+# --------------------------------------------------------------------------------------
+# causal masking (speculative decoding, s_q > 1): the usage example on the geoz.com.cn
+# page passes causal=True; the mask is aligned to the end of the cache, so query token
+# s of s_q sees positions j <= seqlen - s_q + s
+
+
+CAUSAL_CASES = [
+    dict(name="bf16 s_q=3 short and ragged", B=4, s_q=3, h_q=4, seqlens=[1, 2, 64, 200], seed=81),
+    dict(name="fp8 s_q=4", B=2, s_q=4, h_q=3, seqlens=[130, 5], seed=82, is_fp8=True),
+    dict(name="bf16 s_q=2 page edge", B=2, s_q=2, h_q=2, seqlens=[65, 128], seed=83),
+]
+
+
+@pytest.mark.parametrize("case", CAUSAL_CASES, ids=[c["name"] for c in CAUSAL_CASES])
+def test_causal_matches_library_attention(case):
+    c = dict(case)
+    prob = mi.make_problem(c.pop("name"), **c)
+    o, lse = run_oracle(prob, causal=True)
+    o_ref, lse_ref = library_attention(prob, causal=True)
+    for b, L in enumerate(c["seqlens"]):
+        for s in range(prob.s_q):
+            if L - prob.s_q + s < 0:  # the query token sees nothing
+                assert np.all(o[b, s] == 0.0) and np.all(lse[b, s] == -np.inf)
+            else:
+                assert np.allclose(o[b, s], o_ref[b, s].numpy(), rtol=1e-11, atol=1e-12)
+                assert np.allclose(lse[b, s], lse_ref[b, s].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_causal_uniform_scores_give_prefix_mean():
+    L, s_q = 300, 4
+    prob = mi.make_problem("cq0", 1, s_q, 2, [L], seed=84, q_zero=True)
+    o, lse = run_oracle(prob, causal=True)
+    K = library_latents(prob).numpy()
+    for s in range(s_q):
+        n = L - s_q + s + 1
+        pos = np.arange(n)
+        phys = prob.block_table[0].numpy()[pos // 64] * 64 + pos % 64
+        assert np.allclose(o[0, s], K[phys, :512].mean(axis=0), rtol=0, atol=1e-13)
+        assert np.allclose(lse[0, s], math.log(n), rtol=0, atol=1e-13)
+
+
+def test_causal_with_one_query_token_is_the_full_sequence():
+    prob = mi.make_problem("c1", 3, 1, 4, [1, 77, 640], seed=85)
+    oc, lc = run_oracle(prob, causal=True)
+    on, ln = run_oracle(prob)
+    assert np.array_equal(oc, on) and np.array_equal(lc, ln)
+
+
+def test_causal_rejects_sparse():
+    prob = mi.make_problem("cs", 1, 2, 2, [100], seed=86, topk=16)
+    with pytest.raises(ValueError):
+        run_oracle(prob, causal=True)
