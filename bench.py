@@ -196,6 +196,24 @@ def measure(cfg: int, steps: int, warmup: int):
                call_cold_gbps=round(nbytes / (call_cold * 1e-3) / 1e9, 1))
     res["kernel_frac_hbm"] = round(res["kernel_gbps"] / PEAK_HBM_GBS, 4)
     res["kernel_frac_mfma"] = round(res["kernel_tflops"] / PEAK_BF16_TFLOPS, 4)
+    if topk == 0 and prob.s_q > 1:
+        # speculative query tokens with the causal mask (query token s of s_q sees
+        # positions <= seqlen - s_q + s): the same decode kernel, timed the same way
+        ct = mla.DecodeKernelTimer()
+        for _ in range(warmup):
+            mla.mla_decode_with_kvcache(q, kv, bt, sl, 512, meta, idx, prob.is_fp8, prob.softmax_scale, ws, o, lse,
+                                        causal=True)
+        torch.cuda.synchronize()
+        hold_gpu(400.0 * steps + 2000.0)
+        for _ in range(steps):
+            ct.record(lambda: mla.mla_decode_with_kvcache(q, kv, bt, sl, 512, meta, idx, prob.is_fp8,
+                                                          prob.softmax_scale, ws, o, lse, causal=True))
+        cd = ct.durations_ms()
+        c_ms = sum(cd) / len(cd)
+        lens = prob.cache_seqlens.tolist()
+        c_flops = sum(prob.h_q * max(0, L - prob.s_q + s + 1) for L in lens for s in range(prob.s_q)) * 2 * (576 + 512)
+        res["causal_decode_kernel_us"] = round(c_ms * 1e3, 2)
+        res["causal_kernel_tflops"] = round(c_flops / (c_ms * 1e-3) / 1e12, 2)
     del q, kv, bt, sl, idx, ws, o, lse
     torch.cuda.empty_cache()
     return prob, res
@@ -243,6 +261,9 @@ def main():
                   c, prob.name, r["step_us"], r["decode_kernel_us"], r["kernel_tflops"], r["kernel_gbps"],
                   r["decode_call_us_warm_median"], r["decode_call_us_cold_median"], r["scheduler_us"],
                   r["num_workers"], r["splits"]), file=sys.stderr, flush=True)
+        if "causal_decode_kernel_us" in r:
+            print("[bench] config %d causal mask: decode kernel %.1f us (%.1f TFLOP/s)" % (
+                c, r["causal_decode_kernel_us"], r["causal_kernel_tflops"]), file=sys.stderr, flush=True)
         if c == head:
             head_prob = prob
     h = results[head]

@@ -112,6 +112,13 @@ MLA_API int mla_get_metadata(const int32_t* cache_seqlens, int B, int s_q, int h
  *   softmax_scale  <= 0 selects 1 / sqrt(576)
  *   metadata       from mla_get_metadata with the same shape and num_workers
  *   indices        device int32 [B, s_q, topk] when topk > 0, else NULL
+ *   causal         0 or 1; 1 (dense only, else MLA_ERR_INVALID_ARG) masks the
+ *                  attention of speculative query tokens: the s_q query tokens
+ *                  are the last s_q cache positions, so query token s sees
+ *                  positions j <= seqlen_b - s_q + s (none when negative: o = 0,
+ *                  lse = -inf).  The usage example of "FlashMLA: DeepSeek's
+ *                  efficient MLA decoding kernel" passes causal=True for
+ *                  autoregressive decoding.
  *   workspace      device buffer of workspace_bytes (>= the size call's value)
  *   o              device bf16 [B, s_q, h_q, 512] (output)
  *   lse            device fp32 [B, s_q, h_q] (output, natural log)
@@ -125,8 +132,8 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
                                     int max_blocks, const int32_t* cache_seqlens, int B, int s_q, int h_q, int h_kv,
                                     int d_qk, int d_v, float softmax_scale, const int32_t* metadata,
                                     size_t metadata_bytes, int num_workers, const int32_t* indices, int topk,
-                                    int is_fp8, void* workspace, size_t workspace_bytes, void* o, float* lse,
-                                    void* stream);
+                                    int is_fp8, int causal, void* workspace, size_t workspace_bytes, void* o,
+                                    float* lse, void* stream);
 
 /* Thread-local, NUL-terminated description of this thread's last failed call ("" if none). */
 MLA_API const char* mla_last_error(void);

@@ -53,8 +53,8 @@ def lib() -> ctypes.CDLL:
         L.mla_get_metadata.restype = I
         L.mla_get_metadata.argtypes = [P, I, I, I, I, I, I, I, P, Z, P]
         L.mla_decode_with_kvcache.restype = I
-        L.mla_decode_with_kvcache.argtypes = [P, P, I64, P, I, P, I, I, I, I, I, I, ctypes.c_float, P, Z, I, P, I, I, P,
-                                              Z, P, P, P]
+        L.mla_decode_with_kvcache.argtypes = [P, P, I64, P, I, P, I, I, I, I, I, I, ctypes.c_float, P, Z, I, P, I, I, I,
+                                              P, Z, P, P, P]
         L.mla_debug_dequant_fp8.restype = I
         L.mla_debug_dequant_fp8.argtypes = [P, I64, P, P]
         L.mla_set_decode_kernel_events.restype = I
@@ -136,12 +136,15 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
                             indices: Optional[torch.Tensor] = None, is_fp8: bool = False,
                             softmax_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
                             out: Optional[torch.Tensor] = None,
-                            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                            lse: Optional[torch.Tensor] = None,
+                            causal: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """o (bf16 [B, s_q, h_q, 512]) and lse (fp32 [B, s_q, h_q]) of MLA decode.
 
     q: bf16 [B, s_q, h_q, 576]; kvcache: bf16 [num_blocks, 64, (1,) 576] or uint8
     [num_blocks, 64, (1,) 656] with is_fp8; block_table int32 [B, max_blocks];
     cache_seqlens int32 [B]; indices int32 [B, s_q, topk] for sparse decode.
+    causal (dense only): query token s of s_q sees cache positions
+    <= seqlen - s_q + s.
     """
     dev = q.device
     if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[3] != D_QK:
@@ -180,8 +183,8 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
         _check(lib().mla_decode_with_kvcache(
             _ptr(q), _ptr(kvcache), num_blocks, _ptr(block_table), int(block_table.shape[1]), _ptr(cache_seqlens), B,
             s_q, h_q, m.h_kv, D_QK, d_v, scale, _ptr(m.tensor), m.tensor.numel() * 4, m.num_workers, _ptr(indices),
-            topk, int(is_fp8), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
-            _stream(dev)), "mla_decode_with_kvcache")
+            topk, int(is_fp8), int(bool(causal)), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _ptr(out), _ptr(lse), _stream(dev)), "mla_decode_with_kvcache")
     return out, lse
 
 

@@ -148,8 +148,8 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
                                     int max_blocks, const int32_t* cache_seqlens, int B, int s_q, int h_q, int h_kv,
                                     int d_qk, int d_v, float softmax_scale, const int32_t* metadata,
                                     size_t metadata_bytes, int num_workers, const int32_t* indices, int topk,
-                                    int is_fp8, void* workspace, size_t workspace_bytes, void* o, float* lse,
-                                    void* stream) {
+                                    int is_fp8, int causal, void* workspace, size_t workspace_bytes, void* o,
+                                    float* lse, void* stream) {
   g_err[0] = 0;
   if (!q || !kvcache || !block_table || !cache_seqlens || !metadata || !o || !lse || !workspace)
     return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
@@ -157,6 +157,9 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
     return fail(MLA_ERR_UNSUPPORTED, "only d_qk = 576 and d_v = 512 are supported (got %d, %d)", d_qk, d_v);
   if (num_blocks < 1 || max_blocks < 1) return fail(MLA_ERR_INVALID_ARG, "num_blocks and max_blocks must be >= 1");
   if (is_fp8 != 0 && is_fp8 != 1) return fail(MLA_ERR_INVALID_ARG, "is_fp8 must be 0 or 1");
+  if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (causal && topk > 0)
+    return fail(MLA_ERR_INVALID_ARG, "causal masking applies to dense decoding; index lists decide sparse visibility");
   if (topk > 0 && !indices) return fail(MLA_ERR_INVALID_ARG, "topk > 0 needs indices");
   if (topk == 0 && indices) return fail(MLA_ERR_INVALID_ARG, "indices given with topk = 0");
   if ((((uintptr_t)q) | ((uintptr_t)kvcache) | ((uintptr_t)o) | ((uintptr_t)workspace)) & 15)
@@ -195,6 +198,7 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
   p.n_streams = s.n_streams;
   p.n_rt = s.n_rt;
   p.W = W;
+  p.causal = causal;
   p.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = hipSuccess;
   if (g_ev_start && (e = hipEventRecord(g_ev_start, (hipStream_t)stream)) != hipSuccess)

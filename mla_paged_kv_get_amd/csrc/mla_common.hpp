@@ -75,6 +75,7 @@ struct DecodeParams {
   int n_streams;
   int n_rt;                  // row tiles (workgroups) per worker
   int W;                     // workers
+  int causal;                // dense: query token s of s_q sees positions <= seqlen - s_q + s
   float scale_log2;          // softmax_scale * log2(e)
 };
 

@@ -313,14 +313,21 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         return (uint32_t)__ballot(ok);
       }
     };
-    // scores of sub-tile u with the tokens no row attends set to -inf
-    // (this lane: row qrow, tokens 16 tb + 4 h4 + e)
+    // Dense visibility: the tokens [0, vis) a row attends.  Non-causal: the whole
+    // sequence.  Causal: the s_q query tokens are the last s_q positions, so the
+    // row of query token i = row / h_q sees [0, seqlen - s_q + 1 + i) (usage
+    // example of the geoz.com.cn page: causal=True).  vis_min is the smallest
+    // window of the stream (query token 0).
+    const int vis_min = p.causal ? max(seqlen - p.s_q + 1, 0) : seqlen;
+    const int vis_row = p.causal ? min(max(seqlen - p.s_q + 1 + (rt * kRowTile + qrow) / p.h_q, 0), seqlen) : seqlen;
+    // scores of sub-tile u with the tokens this lane's row does not attend set to
+    // -inf (this lane: row qrow, tokens 16 tb + 4 h4 + e)
     auto mask_scores = [&](int u, f32x4& v) {
       const uint32_t tmask = SPARSE ? sparse_mask(u) : 0u;
-      const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= seqlen;
+      const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= vis_min;
       if (!full) {
         asm volatile("");  // a real branch: full sub-tiles skip the masking
-        const int vcount = seqlen - u * kSub;
+        const int vcount = vis_row - u * kSub;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int tok = 16 * tb + 4 * h4 + e;

@@ -27,14 +27,14 @@ def to_device(prob):
     return d
 
 
-def run_gpu(prob, num_workers=0, dev_inputs=None, meta=None):
+def run_gpu(prob, num_workers=0, dev_inputs=None, meta=None, causal=False):
     import mla_paged_kv_get_amd as mla
 
     d = dev_inputs or to_device(prob)
     if meta is None:
         meta = mla.mla_get_metadata(d["cache_seqlens"], prob.s_q, prob.h_q, 1, prob.topk, prob.is_fp8, num_workers)
     o, lse = mla.mla_decode_with_kvcache(d["q"], d["kvcache"], d["block_table"], d["cache_seqlens"], 512, meta,
-                                         d["indices"], prob.is_fp8, prob.softmax_scale)
+                                         d["indices"], prob.is_fp8, prob.softmax_scale, causal=causal)
     torch.cuda.synchronize()
     return o, lse, meta
 
@@ -61,13 +61,13 @@ def compare(o, lse, o_ref, lse_ref, what=""):
     return (float(do.max()) if do.size else 0.0), (float(dl.max()) if dl.size else 0.0)
 
 
-def check_problem(prob, rows=None, num_workers=0, what=None):
+def check_problem(prob, rows=None, num_workers=0, what=None, causal=False):
     """Run on the GPU and compare all rows (rows=None) or a sample with the oracle."""
     what = what or prob.name
-    say("[gpu] %s (W=%s)" % (what, num_workers or "auto"))
-    o, lse, _ = run_gpu(prob, num_workers)
+    say("[gpu] %s (W=%s%s)" % (what, num_workers or "auto", ", causal" if causal else ""))
+    o, lse, _ = run_gpu(prob, num_workers, causal=causal)
     o, lse = flat(o, lse)
-    o_ref, lse_ref = oracle.problem_decode(prob, rows)
+    o_ref, lse_ref = oracle.problem_decode(prob, rows, causal)
     if rows is not None:
         o, lse = o[rows], lse[rows]
     return compare(o, lse, o_ref, lse_ref, what)

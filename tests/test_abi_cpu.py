@@ -78,14 +78,14 @@ def test_size_call_rejects_bad_shapes(L):
 def decode(L, **kw):
     a = dict(q=0x1000, kv=0x2000, num_blocks=4, bt=0x3000, max_blocks=4, sl=0x4000, B=2, s_q=1, h_q=16, h_kv=1,
              d_qk=576, d_v=512, scale=0.0, meta=0x5000, meta_bytes=1 << 20, W=8, idx=None, topk=0, is_fp8=0,
-             ws=0x6000, ws_bytes=1 << 30, o=0x7000, lse=0x8000, stream=None)
+             causal=0, ws=0x6000, ws_bytes=1 << 30, o=0x7000, lse=0x8000, stream=None)
     a.update(kw)
     L.mla_decode_with_kvcache.argtypes = None  # plain ints/None below
     f = L.mla_decode_with_kvcache
     P = ctypes.c_void_p
     return f(P(a["q"]), P(a["kv"]), ctypes.c_int64(a["num_blocks"]), P(a["bt"]), a["max_blocks"], P(a["sl"]), a["B"],
              a["s_q"], a["h_q"], a["h_kv"], a["d_qk"], a["d_v"], ctypes.c_float(a["scale"]), P(a["meta"]),
-             ctypes.c_size_t(a["meta_bytes"]), a["W"], P(a["idx"]), a["topk"], a["is_fp8"], P(a["ws"]),
+             ctypes.c_size_t(a["meta_bytes"]), a["W"], P(a["idx"]), a["topk"], a["is_fp8"], a["causal"], P(a["ws"]),
              ctypes.c_size_t(a["ws_bytes"]), P(a["o"]), P(a["lse"]), P(a["stream"]))
 
 
@@ -97,6 +97,8 @@ def decode(L, **kw):
     (dict(topk=8), -1, "indices"),
     (dict(idx=0x9000), -1, "indices"),
     (dict(is_fp8=2), -1, "is_fp8"),
+    (dict(causal=2), -1, "causal"),
+    (dict(causal=1, topk=8, idx=0x9000), -1, "causal"),
     (dict(q=0x1008), -1, "aligned"),
     (dict(meta_bytes=16), -3, "metadata"),
     (dict(ws_bytes=1024), -3, "workspace"),

@@ -31,4 +31,8 @@ def test_workload_parity(cfg):
     rows = None if SAMPLE[cfg] is None else sample_rows(prob, SAMPLE[cfg], cfg)
     do, dl = check_problem(prob, rows=rows, what="workload %d: %s" % (cfg, prob.name))
     say("[gpu] workload %d max |d o| %.3g max |d lse| %.3g" % (cfg, do, dl))
+    if cfg == 3:
+        # the speculative (s_q = 2) dense workload with the causal mask
+        do, dl = check_problem(prob, rows=rows, what="workload 3 causal", causal=True)
+        say("[gpu] workload 3 causal max |d o| %.3g max |d lse| %.3g" % (do, dl))
     torch.cuda.empty_cache()

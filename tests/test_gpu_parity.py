@@ -249,3 +249,40 @@ def test_lse_merge_through_the_abi():
     o_ref, lse_ref = oracle.problem_decode(prob)
     compare(merged_o, merged_l, o_ref, lse_ref, "merged halves")
     compare(o, lse, o_ref, lse_ref, "whole")
+
+
+# --------------------------------------------------------------------------------------
+# causal masking for speculative query tokens (dense): query token s of s_q sees cache
+# positions <= seqlen - s_q + s
+
+
+CAUSAL = [
+    dict(name="causal bf16 s_q=2 h64, windows of 0 and 1 token", B=4, s_q=2, h_q=64, seqlens=[513, 77, 1, 2], seed=91),
+    dict(name="causal bf16 s_q=4 h32", B=3, s_q=4, h_q=32, seqlens=[200, 3, 64], seed=92),
+    dict(name="causal fp8 s_q=3 h64", B=2, s_q=3, h_q=64, seqlens=[450, 65], seed=93, is_fp8=True),
+    dict(name="causal bf16 s_q=2 h128 (256 rows)", B=2, s_q=2, h_q=128, seqlens=[700, 129], seed=94),
+]
+
+
+@pytest.mark.parametrize("case", CAUSAL, ids=[c["name"] for c in CAUSAL])
+@pytest.mark.parametrize("W", [0, 7])
+def test_causal_parity(case, W):
+    c = dict(case)
+    prob = mi.make_problem(c.pop("name"), **c)
+    check_problem(prob, num_workers=W, causal=True)
+
+
+def test_causal_one_query_token_is_bit_identical_to_noncausal():
+    prob = mi.make_problem("causal s_q=1", 3, 1, 64, [300, 64, 1000], seed=95)
+    d = to_device(prob)
+    o1, l1, _ = run_gpu(prob, 0, dev_inputs=d, causal=True)
+    o0, l0, _ = run_gpu(prob, 0, dev_inputs=d)
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+
+
+def test_causal_rejected_for_sparse():
+    import mla_paged_kv_get_amd as mla
+
+    prob = mi.make_problem("causal sparse", 1, 2, 16, [300], seed=96, topk=64)
+    with pytest.raises(mla.MlaError, match="causal"):
+        run_gpu(prob, 0, causal=True)
