@@ -68,6 +68,20 @@ __device__ __forceinline__ void global_load_lds16(const void* src, MLA_LDS void*
 __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t rs, MLA_LDS void* dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
 }
+__device__ __forceinline__ void global_load_lds4(const void* src, MLA_LDS void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+// Workgroup barrier after waiting for this wave's LDS operations and for all but
+// its N most recently issued vector memory loads (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void barrier_keep() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int V>
+struct Tag {
+  static constexpr int value = V;
+};
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRefLift = 32.0f;   // log2 units
@@ -78,8 +92,8 @@ constexpr int kNBuf = 4;
 // P exchange: [2 (sub-tile parity)][2 row blocks][2 k-steps][64 lanes] bf16x8
 constexpr int kPOffset = kNBuf * kSubBytes;
 constexpr int kPHalf = 2 * 2 * 64 * 16;
-// Metadata: BF16 rings int32 ring_idx[8][64], ring_pg[8][64]; FP8 int32
-// tokidx[8][32] and uint32 vmask[8] in the same space.
+// Metadata rings (per sub-tile, 8 deep): int32 ring_idx[8][64] (sparse slot
+// indices) and ring_pg[8][64] (their pages; dense: the sub-tile's page).
 constexpr int kRing = 8;
 constexpr int kMetaOffset = kPOffset + 2 * kPHalf;
 constexpr int kMetaBytes = 2 * kRing * 64 * 4;
@@ -113,14 +127,13 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
   MLA_LDS char* pbuf = smem + kPOffset;
   MLA_LDS int32_t* ring_idx = (MLA_LDS int32_t*)(smem + kMetaOffset);
   MLA_LDS int32_t* ring_pg = ring_idx + kRing * 64;
-  MLA_LDS int32_t* tokidx = (MLA_LDS int32_t*)(smem + kMetaOffset);
-  MLA_LDS uint32_t* vmask = (MLA_LDS uint32_t*)(tokidx + 8 * kSub);
   MLA_LDS int32_t* wflag = (MLA_LDS int32_t*)(smem + kFlagOffset);
   MLA_LDS float* xrow = (MLA_LDS float*)(smem + kXOffset);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the same, as a scalar
   const int l16 = lane & 15, h4 = lane >> 4;  // 16x16 operand row / k-group
   const int l32 = lane & 31, h2 = lane >> 5;  // 32x32 operand row / k-group
   // scores: rows 16 r4 .., tokens 16 tb .. of each sub-tile
@@ -162,21 +175,18 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
   // V^T operand (transposed reads) of k-step s2, half e4 and the parity of the
   // 32-column block: the 4 lanes of a quad supply tokens 16 s2 + 8 h2 + 4 e4 + q,
   // and each lane receives its column at those 4 tokens; columns 64 wave ..
-  int vofs[2][2][2];
+  // The swizzle of those tokens depends on bits 1 and 3 only (q and h2), so
+  // s2 and e4 add the constant 1152 (16 s2 + 4 e4): vofs holds s2 = e4 = 0.
+  int vofs[2];
   {
     const int q = (lane & 15) >> 2;
     const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int e4 = 0; e4 < 2; ++e4) {
-        const int tok = 16 * s2 + 8 * h2 + 4 * e4 + q;
-        const int sw = tile_swizzle(tok);
-        const int sb = sw >> 2;
-        const int base = tok * kBf16TokenBytes + 128 * wave + ((cl ^ (sw & 3)) << 4) + 8 * (lane & 1);
-        vofs[s2][e4][0] = base + 64 * sb;
-        vofs[s2][e4][1] = base - 64 * sb;
-      }
+    const int tok = 8 * h2 + q;
+    const int sw = tile_swizzle(tok);
+    const int sb = sw >> 2;
+    const int base = tok * kBf16TokenBytes + 128 * wave + ((cl ^ (sw & 3)) << 4) + 8 * (lane & 1);
+    vofs[0] = base + 64 * sb;
+    vofs[1] = base - 64 * sb;
   }
   // P block of this lane (row qrow, tokens 16 tb + 4 h4 + e) in the layout the
   // PV step reads: [row block qrow / 32][k-step tb][lane 16 (r4 & 1) + l16 + 32 (h4 / 2)]
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
 
     const int b = SPARSE ? stream / p.s_q : stream;
     const int64_t row_base = (int64_t)stream * p.R_stream;
-    const int seqlen = p.seqlens[b];
+    const int seqlen = __builtin_amdgcn_readfirstlane(p.seqlens[b]);  // uniform: keeps what derives from it scalar
     const int32_t* bt_row = p.block_table + (int64_t)b * p.max_blocks;
     const int32_t* idx_row = SPARSE ? p.indices + (int64_t)stream * p.topk : nullptr;
     const __amdgpu_buffer_rsrc_t bt_rs =
@@ -214,9 +224,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     // Q fragments (B operand of the score MFMA): row qrow, dims 32 kk + 8 h4 ..
     bf16x8 qf[18];
     {
-      const int row = rt * kRowTile + qrow;
+      int lo = lane;
+      asm volatile("" : "+v"(lo));  // the row pointer is formed here, not kept live across pieces
+      const int row = rt * kRowTile + 16 * r4 + (lo & 15);
       const bool row_ok = row < p.R_stream;
-      const uint16_t* qr = p.q + (row_base + (row_ok ? row : 0)) * kDQK + 8 * h4;
+      const uint16_t* qr = p.q + (row_base + (row_ok ? row : 0)) * kDQK + 8 * (lo >> 4);
 #pragma unroll
       for (int kk = 0; kk < 18; ++kk) {
         u32x4 v = *(const u32x4*)(qr + 32 * kk);
@@ -229,89 +241,62 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     f32x16 acc[2][2];
 
     // ---- per sub-tile metadata ----------------------------------------------------
-    // Round u (below) streams sub-tile u + 2 into LDS; whatever it needs to know
-    // about a sub-tile (its cache page, or the token rows of its 32 index slots)
-    // was fetched rounds ahead into LDS, so no round waits on a load it just issued.
-    //
-    // BF16 (tiles arrive by direct global->LDS loads): the metadata travels the
-    // same way, into rings of 8 sub-tiles, issued by wave 0 at the start of a
-    // round and landed by its end.  Round u fetches the page of sub-tile u + 3
-    // (dense), or the indices of sub-tile u + 4 and the pages of sub-tile u + 3's
-    // indices (sparse).  No loaded value ever lands in a register inside the
-    // loop: the compiler could only wait for such a value by draining every
-    // direct load still streaming.
-    //
-    // FP8 (tiles go through registers): sub-tile u's metadata sits in LDS slot
-    // u & 7 (dense: its page; sparse: the token row of each slot, -1 when not
-    // attended, and the attended mask); every wave loads the metadata of sub-tile
-    // u + 4 during round u and wave 0 publishes it at the end of the round.
+    // Round u issues the tile loads of sub-tile u + 3 (BF16: direct global->LDS
+    // loads, waited for at the end of the next round; FP8: loads into VGPRs,
+    // dequantised into LDS in the next round).  What a round needs to know about a
+    // sub-tile (its cache page, or the index and page of each of its 32 slots) was
+    // fetched earlier by direct loads into LDS rings of 8 sub-tiles, issued by
+    // wave 0: round u fetches the page of sub-tile u + 5 (dense), or the indices of
+    // sub-tile u + 7 and the pages of sub-tile u + 5's indices (sparse); such a
+    // load has landed and is visible two rounds later.  No loaded value ever lands
+    // in a register it has to carry across rounds: the compiler could only wait
+    // for it by draining every load still streaming.
     auto slot_ok = [&](int u) { return u < u1 && u * kSub + l32 < p.topk; };  // sparse slot l32 exists
-    // BF16 direct metadata loads (64 lanes each; lanes 32..63 repeat 0..31)
-    auto meta_dma = [&](int u) {
+    // Direct metadata loads into the rings (64 lanes each; lanes 32..63 repeat
+    // 0..31): the indices of sub-tile x, the pages of sub-tile x's indices
+    // (sparse; its indices must be visible), the page of sub-tile x (dense; the
+    // split's last page past its end).
+    auto fetch_idx = [&](int x) {
+      const int si = min(x * kSub + l32, p.topk - 1);
+      global_load_lds4((const void*)(idx_row + si), (MLA_LDS void*)(ring_idx + (x & (kRing - 1)) * 64));
+    };
+    auto fetch_pg = [&](int x) {
+      const int idx = ring_idx[(x & (kRing - 1)) * 64 + l32];
+      const bool ok = slot_ok(x) && idx >= 0;
+      global_load_lds4((const void*)(bt_row + (ok ? idx >> 6 : 0)), (MLA_LDS void*)(ring_pg + (x & (kRing - 1)) * 64));
+    };
+    auto fetch_page = [&](int x) {
+      buffer_load_lds4(bt_rs, (MLA_LDS void*)(ring_pg + (x & (kRing - 1)) * 64), (uint32_t)(min(x, u1 - 1) >> 1) * 4u);
+    };
+    // round u's share: sparse part 0 the indices of sub-tile u + 7, part 1 the
+    // pages of sub-tile u + 5; dense the page of sub-tile u + 5
+    auto meta_dma = [&](int u, int part) {
       if constexpr (SPARSE) {
-        // indices of sub-tile u + 4
-        const int si = min((u + 4) * kSub + l32, p.topk - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(idx_row + si),
-                                         (MLA_LDS void*)(ring_idx + ((u + 4) & (kRing - 1)) * 64), 4, 0, 0);
-        // pages of sub-tile u + 3's indices
-        const int idx = ring_idx[((u + 3) & (kRing - 1)) * 64 + l32];
-        const bool ok = slot_ok(u + 3) && idx >= 0;
-        __builtin_amdgcn_global_load_lds((const void*)(bt_row + (ok ? idx >> 6 : 0)),
-                                         (MLA_LDS void*)(ring_pg + ((u + 3) & (kRing - 1)) * 64), 4, 0, 0);
+        if (part == 0)
+          fetch_idx(u + 7);
+        else
+          fetch_pg(u + 5);
       } else {
-        // page of sub-tile u + 3 (the split's last page past its end)
-        buffer_load_lds4(bt_rs, (MLA_LDS void*)(ring_pg + ((u + 3) & (kRing - 1)) * 64),
-                         (uint32_t)(min(u + 3, u1 - 1) >> 1) * 4u);
+        fetch_page(u + 5);
       }
     };
-    // BF16 prologue: the same ring entries by plain loads (indices of u0 .. u0 + 3,
-    // pages of u0 .. u0 + 2)
+    // prologue: the ring entries of sub-tiles u0 .. u0 + 4 (pages) and, sparse,
+    // u0 .. u0 + 6 (indices), one sub-tile per wave; ends with a barrier after
+    // which they are visible
     auto meta_fill = [&]() {
-      if (wave == 0) {
-        if constexpr (SPARSE) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int u = u0 + j;
-            const int idx = idx_row[min(u * kSub + l32, p.topk - 1)];
-            ring_idx[(u & (kRing - 1)) * 64 + lane] = idx;
-            if (j < 3) {
-              const bool ok = slot_ok(u) && idx >= 0;
-              ring_pg[(u & (kRing - 1)) * 64 + lane] = bt_row[ok ? idx >> 6 : 0];
-            }
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 3; ++j) {
-            const int u = u0 + j;
-            ring_pg[(u & (kRing - 1)) * 64 + lane] = bt_row[min(u, u1 - 1) >> 1];
-          }
-        }
+      if constexpr (SPARSE) {
+        if (wave_s < 7) fetch_idx(u0 + wave_s);
+        tile_barrier_drain();
+        if (wave_s < 5) fetch_pg(u0 + wave_s);
+      } else {
+        if (wave_s < 5) fetch_page(u0 + wave_s);
       }
-    };
-    // FP8 metadata (plain loads)
-    auto idx_at = [&](int u) -> int { return slot_ok(u) ? idx_row[u * kSub + l32] : -1; };
-    auto tok_of = [&](int idx) -> int {
-      const int pg = bt_row[(idx < 0 ? 0 : idx) >> 6];  // always issued
-      return idx >= 0 ? pg * kPage + (idx & 63) : -1;
-    };
-    auto page_load = [&](int u) -> int { return bt_row[min(u, u1 - 1) >> 1]; };
-    auto publish = [&](int u, int v) {  // wave 0
-      if (SPARSE) {
-        const uint64_t m = __ballot(v >= 0);
-        if (lane < kSub) tokidx[(u & 7) * kSub + lane] = v;
-        if (lane == 0) vmask[u & 7] = (uint32_t)m;
-      } else if (lane == 0) {
-        tokidx[(u & 7) * kSub] = v;
-      }
+      tile_barrier_drain();
     };
     // attended mask of sub-tile u's 32 slots (sparse)
     auto sparse_mask = [&](int u) -> uint32_t {
-      if constexpr (FP8) {
-        return vmask[u & 7];
-      } else {
-        const bool ok = slot_ok(u) && ring_idx[(u & (kRing - 1)) * 64 + l32] >= 0;
-        return (uint32_t)__ballot(ok);
-      }
+      const bool ok = slot_ok(u) && ring_idx[(u & (kRing - 1)) * 64 + l32] >= 0;
+      return (uint32_t)__ballot(ok);
     };
     // Dense visibility: the tokens [0, vis) a row attends.  Non-causal: the whole
     // sequence.  Causal: the s_q query tokens are the last s_q positions, so the
@@ -327,78 +312,112 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= vis_min;
       if (!full) {
         asm volatile("");  // a real branch: full sub-tiles skip the masking
-        const int vcount = vis_row - u * kSub;
+        // tok0 is made opaque so that the compiler does not keep 4 token numbers
+        // live across the loop
+        int tok0 = 16 * tb + 4 * h4;
+        asm volatile("" : "+v"(tok0));
+        const int vcount = vis_row - u * kSub - tok0;
+        const uint32_t lmask = tmask >> tok0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int tok = 16 * tb + 4 * h4 + e;
-          const bool ok = SPARSE ? ((tmask >> tok) & 1u) != 0 : tok < vcount;
+          const bool ok = SPARSE ? ((lmask >> e) & 1u) != 0 : e < vcount;
           v[e] = ok ? v[e] : kNegInf;
         }
       }
     };
     // ---- staging ------------------------------------------------------------------
-    auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((u - u0 + kNBuf) % kNBuf) * kSubBytes; };
-    // FP8: byte address of stored token t of sub-tile u (the zero token when not attended)
-    auto token_ptr = [&](int u, int t) -> const uint8_t* {
+    auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((unsigned)(u - u0) & (kNBuf - 1)) * kSubBytes; };
+    // FP8: byte address of stored token t of sub-tile u (the zero token when not
+    // attended), from its ring entries (sparse: idx, pg; dense: the page), which
+    // the caller reads first for all of its tokens, so their LDS latencies overlap.
+    auto token_ptr = [&](int u, int t, int idx, int pg) -> const uint8_t* {
       if (SPARSE) {
-        const int tok = tokidx[(u & 7) * kSub + t];
-        return tok >= 0 ? p.kv + (int64_t)tok * tok_bytes : g_zero_token;
+        const bool ok = u < u1 && u * kSub + t < p.topk && idx >= 0;
+        return ok ? p.kv + ((int64_t)pg * kPage + (idx & 63)) * tok_bytes : g_zero_token;
       }
-      if (u * kSub + t >= seqlen) return g_zero_token;
-      const int page = tokidx[(u & 7) * kSub];
-      return p.kv + ((int64_t)page * kPage + (u & 1) * kSub + t) * tok_bytes;
+      // past the split the ring slot may never have been written: its page is not used
+      if (u >= u1 || u * kSub + t >= seqlen) return g_zero_token;
+      return p.kv + ((int64_t)pg * kPage + (u & 1) * kSub + t) * tok_bytes;
     };
     // BF16 direct loads of sub-tile u: this thread's five (or four) 16-byte
-    // pieces, each issued as soon as its address is known (no address arrays:
-    // registers are scarce).  Dense tiles use buffer loads against the
-    // sub-tile's 36,864 bytes, and tokens past the sequence end take an
-    // out-of-range offset, which loads zeros; sparse tiles load from per-lane
-    // global addresses (the zero token when a slot is not attended).
-    auto stage_bf16 = [&](int u, MLA_LDS char* buf) {
+    // pieces.  Dense tiles use buffer loads against a resource that covers only
+    // the sub-tile's tokens inside the sequence, so the pieces of tokens past
+    // its end load zeros; sparse tiles load from per-lane global addresses (the
+    // zero token when a slot is not attended).  stage_begin reads the
+    // sub-tile's ring entry; stage_load issues piece k.
+    __amdgpu_buffer_rsrc_t st_rs;  // dense: the sub-tile's bytes inside the sequence
+    int st_tok = -1;               // sparse: token row of slot l32
+    auto stage_begin = [&](int u) {
       const int r = (u & (kRing - 1)) * 64;
-      auto dst = [&](int k) { return (MLA_LDS void*)(buf + k * (kDecThreads * 16) + wave * 1024); };
       if constexpr (SPARSE) {
-        // token row of slot l32, then of each load's token
         const int idx = ring_idx[r + l32];
         const int pg = ring_pg[r + l32];
-        const int tok = (slot_ok(u) && idx >= 0) ? pg * kPage + (idx & 63) : -1;
-#pragma unroll
-        for (int k = 0; k < kLoads; ++k) {
-          if (k == kLoads - 1 && wave >= 4) break;
-          const int t = slot_token(k);
-          const int tk = __shfl(tok, t);
-          const uint8_t* src = (tk >= 0 ? p.kv + (int64_t)tk * kBf16TokenBytes : g_zero_token) + slot_src(k, t);
-          global_load_lds16((const void*)src, dst(k));
-        }
+        st_tok = (slot_ok(u) && idx >= 0) ? pg * kPage + (idx & 63) : -1;
       } else {
         const int page = __builtin_amdgcn_readfirstlane(ring_pg[r]);
         const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, kSubBytes, kBufferFlags);
-        const int valid = seqlen - u * kSub;  // tokens of the sub-tile inside the sequence
-#pragma unroll
-        for (int k = 0; k < kLoads; ++k) {
-          if (k == kLoads - 1 && wave >= 4) break;
-          const int t = slot_token(k);
-          buffer_load_lds16(rs, dst(k), t < valid ? (uint32_t)(t * kBf16TokenBytes + slot_src(k, t)) : (uint32_t)kSubBytes);
-        }
+        // tokens inside the sequence (scalar: the resource must be uniform)
+        const int valid = __builtin_amdgcn_readfirstlane(min(max(seqlen - u * kSub, 0), kSub));
+        st_rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, valid * kBf16TokenBytes, kBufferFlags);
       }
+    };
+    auto stage_load = [&](int k, MLA_LDS char* buf) {  // k < kLoads - 1, or waves 0..3
+      MLA_LDS void* dst = (MLA_LDS void*)(buf + k * (kDecThreads * 16) + wave_s * 1024);
+      if constexpr (SPARSE) {
+        // the piece's token and source offset, recomputed from an opaque copy of
+        // tid rather than kept live across the loop
+        int to = tid;
+        asm volatile("" : "+v"(to));
+        const int s = min(k * kDecThreads + to, kSlots - 1);
+        const int tt = s / kTokenChunks;
+        const int tk = __shfl(st_tok, tt);
+        const uint8_t* src = (tk >= 0 ? p.kv + (int64_t)tk * kBf16TokenBytes : g_zero_token) +
+                             ((s - tt * kTokenChunks) ^ tile_swizzle(tt)) * 16;
+        global_load_lds16((const void*)src, dst);
+      } else {
+        const int t = slot_token(k);
+        buffer_load_lds16(st_rs, dst, (uint32_t)(t * kBf16TokenBytes + slot_src(k, t)));
+      }
+    };
+    auto stage_bf16 = [&](int u, MLA_LDS char* buf) {
+      stage_begin(u);
+#pragma unroll
+      for (int k = 0; k < kLoads - 1; ++k) stage_load(k, buf);
+      if (wave_s < 4) stage_load(kLoads - 1, buf);
     };
     auto load_fp8 = [&](int u, RawFp8& r) {
+      const int rs = (u & (kRing - 1)) * 64;
+      int lo = lane;
+      asm volatile("" : "+v"(lo));  // per-lane offsets recomputed here, not kept live
+      const int tr = 8 * wave_s + (lo >> 3);  // waves 0..3: the token of this lane's RoPE chunk
+      int ix[5], pg[5];
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        const int t = k < 4 ? 8 * k + wave_s : tr;
+        ix[k] = SPARSE ? ring_idx[rs + t] : 0;
+        pg[k] = ring_pg[SPARSE ? rs + t : rs];
+      }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint8_t* pt = token_ptr(u, 8 * k + wave);
-        r.v[k] = *(const u32x2*)(pt + 8 * lane);
-        r.sc[k] = *(const float*)(pt + kFp8Dims + 4 * (lane >> 4));
+        const uint8_t* pt = token_ptr(u, 8 * k + wave_s, ix[k], pg[k]);
+        r.v[k] = *(const u32x2*)(pt + 8 * lo);
+        r.sc[k] = *(const float*)(pt + kFp8Dims + 4 * (lo >> 4));
       }
-      if (wave < 4) r.r = *(const u32x4*)(token_ptr(u, tid >> 3) + kFp8Dims + 16 + 16 * (tid & 7));
+      if (wave_s < 4) r.r = *(const u32x4*)(token_ptr(u, tr, ix[4], pg[4]) + kFp8Dims + 16 + 16 * (lo & 7));
     };
+    // Token 8 k + wave's swizzle is 4 bit1(wave) + 2 (k & 1), so the store
+    // address of chunk `lane` is one of two per-lane bases plus 8 k token rows.
     auto store_fp8 = [&](const RawFp8& r, MLA_LDS char* buf) {
+      int lo = lane;
+      asm volatile("" : "+v"(lo));  // recomputed here rather than kept live across the loop
+      const int b0 = (wave_s * kTokenChunks + (lo ^ (4 * ((wave_s >> 1) & 1)))) * 16;
+      const int b1 = (wave_s * kTokenChunks + (lo ^ (4 * ((wave_s >> 1) & 1) + 2))) * 16;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const u32x2 a = dequant4(r.v[k].x, r.sc[k]), b = dequant4(r.v[k].y, r.sc[k]);
-        *(MLA_LDS u32x4*)(buf + tile_slot(8 * k + wave, lane) * 16) = u32x4{a.x, a.y, b.x, b.y};
+        *(MLA_LDS u32x4*)(buf + ((k & 1) ? b1 : b0) + 8 * k * kBf16TokenBytes) = u32x4{a.x, a.y, b.x, b.y};
       }
-      if (wave < 4) *(MLA_LDS u32x4*)(buf + tile_slot(tid >> 3, 64 + (tid & 7)) * 16) = r.r;
+      if (wave_s < 4) *(MLA_LDS u32x4*)(buf + tile_slot(8 * wave_s + (lo >> 3), 64 + (lo & 7)) * 16) = r.r;
     };
     // ---- operand reads ------------------------------------------------------------
     auto kread = [&](MLA_LDS char* kb, int kk) -> bf16x8 {
@@ -406,8 +425,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     };
     // V^T fragment: 32-column block ct of this wave's 64 columns, 16-token k-step s2
     auto vread = [&](MLA_LDS char* vb, int s2, int ct) -> bf16x8 {
-      const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(vb + vofs[s2][0][ct & 1] + 64 * ct));
-      const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(vb + vofs[s2][1][ct & 1] + 64 * ct));
+      const int o = vofs[ct & 1] + 64 * ct + 16 * s2 * kBf16TokenBytes;
+      const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(vb + o));
+      const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(vb + o + 4 * kBf16TokenBytes));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     // P fragment (B operand of PV): row block rb, k-step s2 of the sub-tile of parity par
@@ -432,46 +452,55 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     float m_ref = kNegInf, m_seen = kNegInf, l_sum = 0.f;
     bool redo = false;
     int pass = 0;  // at most two: the second pass runs with the split's row maximum
+    constexpr int kAhead = 4;   // K fragments read ahead of their score MFMA
+    constexpr int kPRead = 13;  // score MFMA after which the P fragments are read
     do {
       l_sum = 0.f;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[rb][ct][e] = 0.f;
       bool overflow = false;
 
-      // ---- prologue: metadata, sub-tiles u0 and u0 + 1 in LDS, S of u0 ------------
-      int idx_pref = -1;  // FP8 sparse: index of slot l32 of sub-tile u + 4
-      RawFp8 raw;         // FP8: sub-tile u + 2 in flight in VGPRs
+      // ---- prologue ---------------------------------------------------------------
+      // BF16: sub-tiles u0 .. u0 + 2 issued, u0 and u0 + 1 landed.  FP8: u0 and
+      // u0 + 1 stored, u0 + 2 in flight in VGPRs.  Then S of u0 and the reference.
+      RawFp8 raw;  // FP8: the next sub-tile to store, in VGPRs
       if constexpr (FP8) {
-        int v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = SPARSE ? tok_of(idx_at(u0 + j)) : page_load(u0 + j);
-        if (SPARSE) idx_pref = idx_at(u0 + 4);
-        if (wave == 0)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) publish(u0 + j, v[j]);
-        __syncthreads();
-        load_fp8(u0, raw);
-        store_fp8(raw, buffer(u0));
-        load_fp8(u0 + 1, raw);
-        store_fp8(raw, buffer(u0 + 1));
+        meta_fill();
+        {
+          RawFp8 r1;
+          load_fp8(u0, raw);
+          load_fp8(u0 + 1, r1);
+          store_fp8(raw, buffer(u0));
+          store_fp8(r1, buffer(u0 + 1));
+        }
         load_fp8(u0 + 2, raw);
-        __syncthreads();
+        lds_barrier();
       } else {
         meta_fill();
-        __syncthreads();
         stage_bf16(u0, buffer(u0));
-        stage_bf16(u0 + 1, buffer(u0 + 1));
-        tile_barrier_drain();
+        if (u0 + 1 < u1) stage_bf16(u0 + 1, buffer(u0 + 1));
+        if (u0 + 2 < u1) {
+          stage_bf16(u0 + 2, buffer(u0 + 2));
+          // sub-tiles u0 and u0 + 1 landed; u0 + 2 (5 or 4 loads) stays in flight
+          if (wave_s < 4)
+            barrier_keep<kLoads>();
+          else
+            barrier_keep<kLoads - 1>();
+        } else {
+          tile_barrier_drain();
+        }
       }
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};  // S^T of the sub-tile whose softmax comes next
+      // K fragments kk .. kk + kAhead - 1 of the next score step (rolling)
+      bf16x8 kf[kAhead];
+      f32x4 s;  // S^T of the sub-tile whose softmax comes next
       {
         MLA_LDS char* kb = buffer(u0);
 #pragma unroll
-        for (int kk = 0; kk < 18; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kread(kb, kk), qf[kk], s, 0, 0, 0);
+        for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kb, kk);
+        s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) {
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk % kAhead], qf[kk], s, 0, 0, 0);
+          if (kk + kAhead < 18) kf[kk % kAhead] = kread(kb, kk + kAhead);
+        }
       }
       if (!redo) {
         // the reference of each row from sub-tile u0 (both token blocks of the row)
@@ -480,41 +509,97 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
         mx = row_max16(mx);
         if (h4 == 0) xrow[tb * 64 + qrow] = mx;
-        __syncthreads();
+        lds_barrier();
         const float m0 = fmaxf(xrow[qrow], xrow[64 + qrow]) * p.scale_log2;
         m_ref = m0 == kNegInf ? kNegInf : m0 + kRefLift;
-        __syncthreads();
+        // xrow is next written after the loop, behind at least one round's barrier
       }
 
-      // One round u: softmax of sub-tile u (its P to LDS), PV of sub-tile u - 1
-      // (V^T from vb), QK of sub-tile u + 1 (K from kb), while sub-tile u + 2
-      // streams into nxt.  The buffers are distinct, and saying so (restrict) lets
-      // the compiler keep the direct loads in flight across the reads of vb and kb.
-      auto round = [&](const int u, MLA_LDS char* __restrict__ vb, MLA_LDS char* __restrict__ kb,
-                       MLA_LDS char* __restrict__ nxt) __attribute__((always_inline)) {
-        const bool pv = u > u0;  // workgroup-uniform
-        int meta = 0;  // FP8: metadata of sub-tile u + 4 (published at the end of this round)
-        if constexpr (FP8) {
-          if (SPARSE) {
-            meta = tok_of(idx_pref);
-            idx_pref = idx_at(u + 5);
+      // (zeroed here, after the prologue's loads, not before them)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[rb][ct][e] = 0.f;
+      // V^T fragments of the sub-tile whose PV comes next (read before the barrier
+      // that precedes that PV)
+      bf16x8 va[2][2];
+      // One round u, entered after the barrier that ended round u - 1, with S(u)
+      // in s (round u0: from the prologue), the first K fragments of sub-tile u in
+      // kf, V^T of sub-tile u - 1 in va and P of sub-tile u - 1 in LDS:
+      //   scores of sub-tile u (round u0: computed already), with the staging of a
+      //   later sub-tile (BF16: direct loads of u + 3; FP8: store of u + 2, loads
+      //   of u + 3) between the MFMAs;
+      //   O += P V of sub-tile u - 1, with the softmax of sub-tile u, its P write
+      //   and the V^T reads of sub-tile u between the MFMAs;
+      //   the first K fragments of sub-tile u + 1; one barrier.
+      // So every MFMA operand a round needs after its barrier is in VGPRs or was
+      // written before it, and the LDS and VALU work sits between MFMAs.  The
+      // buffers are distinct, and saying so (restrict) lets the compiler keep the
+      // direct loads in flight across the reads of kb and kn.
+      // Compile-time knobs: kFirst (round u0); kIssue = 1 when sub-tile u + 3 is
+      // known to exist (the main loop), -1 when that is decided at run time.
+      // BF16 load accounting: a round that stages issues exactly kLoads vector
+      // memory operations per wave (waves 0..3 five tile pieces, waves 4..7 four
+      // and one metadata load), so its closing wait is one count for every wave.
+      auto round = [&](auto first_tag, auto issue_tag, const int u, MLA_LDS char* __restrict__ kb,
+                       MLA_LDS char* __restrict__ kn, MLA_LDS char* __restrict__ nxt) __attribute__((always_inline)) {
+        constexpr bool kFirst = decltype(first_tag)::value != 0;
+        constexpr int kIssue = decltype(issue_tag)::value;
+        const bool issue = kIssue == 1 || u + 3 < u1;  // sub-tile u + 3 exists (workgroup-uniform)
+        __builtin_amdgcn_sched_barrier(0);
+        // staging work placed after score MFMA kk
+        auto stage_step = [&](int kk) __attribute__((always_inline)) {
+          if constexpr (FP8) {
+            // The loads into VGPRs are issued whether or not their sub-tile exists
+            // (past the split they read in-bounds bytes that are never used), so
+            // that the compiler's wait for them is a count on every path.
+            if (kk == 1) {
+              store_fp8(raw, nxt);
+              // every load issued before this round (the metadata included) has
+              // landed; the round's barrier publishes it
+              asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            if (kk == 2 && wave_s == 0 && issue) {
+              meta_dma(u, 0);
+              if (SPARSE) meta_dma(u, 1);
+            }
+            if (kk == 3) load_fp8(u + 3, raw);
           } else {
-            meta = page_load(u + 4);
+            if (issue) {
+              if (kk == 0) stage_begin(u + 3);
+              if (kk % 3 == 1 && kk / 3 < kLoads - 1) stage_load(kk / 3, nxt);
+              if (kk == 3 * (kLoads - 1) + 1) {
+                if (wave_s < 4)
+                  stage_load(kLoads - 1, nxt);
+                else  // dense: waves 4..7 load the same page; sparse: 4, 5 part 0, 6, 7 part 1
+                  meta_dma(u, (wave_s >> 1) & 1);
+              }
+            }
+          }
+        };
+        bf16x8 pp[2][2];  // P of sub-tile u - 1, read while the last score MFMAs run
+        if constexpr (!kFirst) {
+          s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 18; ++kk) {
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk % kAhead], qf[kk], s, 0, 0, 0);
+            if (kk + kAhead < 18) kf[kk % kAhead] = kread(kb, kk + kAhead);
+            if (kk == kPRead)
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) pp[rb][s2] = pread((u - 1) & 1, rb, s2);
+            stage_step(kk);
+            __builtin_amdgcn_sched_barrier(0);
           }
         } else {
-          if (wave == 0) meta_dma(u);
+#pragma unroll
+          for (int kk = 0; kk < 18; ++kk) stage_step(kk);
         }
-        __builtin_amdgcn_sched_barrier(0);  // metadata loads stay ahead of the tile loads
-        // sub-tile u + 2: direct loads (BF16) or the registers loaded last round (FP8)
-        if constexpr (FP8) {
-          store_fp8(raw, nxt);
-          load_fp8(u + 3, raw);
-        } else {
-          stage_bf16(u + 2, nxt);
-        }
-        __builtin_amdgcn_sched_barrier(0);
         // softmax of sub-tile u: P = 2^(scale_log2 S - m_ref)
-        {
+        auto softmax = [&]() __attribute__((always_inline)) {
           f32x4 v = s;
           mask_scores(u, v);
           const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])) * p.scale_log2;
@@ -532,61 +617,48 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
           p23.y = (__bf16)pe[3];
           *(MLA_LDS u32x2*)(pbuf + (u & 1) * kPHalf + pw_off) =
               u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-        }
-        // PV(u - 1): O^T += V^T P^T, P of every wave, V^T of this wave's columns
-        if (pv) {
-          bf16x8 pp[2][2], va[2][2];
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) pp[rb][s2] = pread((u - 1) & 1, rb, s2);
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) va[s2][ct] = vread(vb, s2, ct);
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-              for (int ct = 0; ct < 2; ++ct)
-                acc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s2][ct], pp[rb][s2], acc[rb][ct], 0, 0, 0);
-        }
-        // QK(u + 1), K fragments read kAhead steps ahead
-        constexpr int kAhead = 4;
-        bf16x8 kf[18];
-#pragma unroll
-        for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kb, kk);
-        __builtin_amdgcn_sched_barrier(0);
-        s = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-          if (kk + kAhead < 18) kf[kk + kAhead] = kread(kb, kk + kAhead);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (FP8) {
-          if (wave == 0) publish(u + 4, meta);
-          lds_barrier();  // sub-tile u + 2 went through registers
-        } else {
-          tile_barrier_drain();  // sub-tile u + 2 and the metadata have landed
-        }
-      };
-      for (int u = u0; u < u1; ++u) round(u, buffer(u - 1), buffer(u + 1), buffer(u + 2));
-
-      // PV of the last sub-tile
-      {
-        const int u = u1;
-        MLA_LDS char* vb = buffer(u - 1);
-        bf16x8 pp[2][2], va[2][2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) pp[rb][s2] = pread((u - 1) & 1, rb, s2);
+        };
+        // PV(u - 1): O^T += V^T P^T (P of every wave, V^T of this wave's columns);
+        // each V^T fragment is replaced by sub-tile u's once its two MFMAs issued
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) va[s2][ct] = vread(vb, s2, ct);
+          for (int ct = 0; ct < 2; ++ct) {
+            if constexpr (!kFirst) {
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb)
+                acc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s2][ct], pp[rb][s2], acc[rb][ct], 0, 0, 0);
+            }
+            va[s2][ct] = vread(kb, s2, ct);
+            if (s2 == 0 && ct == 0) softmax();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        // the first K fragments of sub-tile u + 1
+        if (kIssue == 1 || u + 1 < u1)
+#pragma unroll
+          for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kn, kk);
+        if constexpr (FP8) {
+          lds_barrier();  // sub-tile u + 2 went through registers
+        } else if (issue) {
+          barrier_keep<kLoads>();  // the previous round's loads (sub-tile u + 2, metadata) have landed
+        } else {
+          tile_barrier_drain();
+        }
+      };
+      constexpr int kStageAhead = FP8 ? 2 : 3;  // the sub-tile a round stages
+      round(Tag<1>{}, Tag<-1>{}, u0, buffer(u0), buffer(u0 + 1), buffer(u0 + kStageAhead));
+      int u = u0 + 1;
+      // main loop: every round stages an existing sub-tile; then the last rounds
+      for (; u + 3 < u1; ++u) round(Tag<0>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+      for (; u < u1; ++u) round(Tag<0>{}, Tag<-1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+
+      // PV of the last sub-tile
+      {
+        bf16x8 pp[2][2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) pp[rb][s2] = pread((u1 - 1) & 1, rb, s2);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
