@@ -92,11 +92,12 @@ constexpr int kNBuf = 4;
 // P exchange: [2 (sub-tile parity)][2 row blocks][2 k-steps][64 lanes] bf16x8
 constexpr int kPOffset = kNBuf * kSubBytes;
 constexpr int kPHalf = 2 * 2 * 64 * 16;
-// Metadata rings (per sub-tile, 8 deep): int32 ring_idx[8][64] (sparse slot
-// indices) and ring_pg[8][64] (their pages; dense: the sub-tile's page).
-constexpr int kRing = 8;
+// Metadata rings (per sub-tile): int32 ring_idx[16][64] (sparse slot indices)
+// and ring_pg[8][64] (their pages; dense: the sub-tile's page).
+constexpr int kRingIdx = 16;
+constexpr int kRingPg = 8;
 constexpr int kMetaOffset = kPOffset + 2 * kPHalf;
-constexpr int kMetaBytes = 2 * kRing * 64 * 4;
+constexpr int kMetaBytes = (kRingIdx + kRingPg) * 64 * 4;
 constexpr int kFlagOffset = kMetaOffset + kMetaBytes;  // int32 per-wave flags[8]
 constexpr int kXOffset = kFlagOffset + 64;             // float row exchange [3][64]
 constexpr int kLdsBytes = kXOffset + 3 * 64 * 4;
@@ -110,14 +111,15 @@ static_assert(kSlots == 4 * kDecThreads + kDecThreads / 2, "staging split");
 constexpr int kBufferFlags = 0x00020000;
 
 // FP8 registers of one sub-tile for this thread: for k = 0..3 the 8 codes of
-// dims 8 lane .. of token 8 k + wave and their scale (scale lane / 16), and for
-// waves 0..3 the RoPE chunk tid % 8 (dims 512 + 8 (tid % 8) ..) of token tid / 8.
-// A wave thus dequantises 64 consecutive 16-byte chunks of one token per store
-// (conflict-free LDS writes) from 512 consecutive code bytes.
+// dims 8 lane .. of token 8 k + wave and their scale (scale lane / 16), and 8
+// bytes of RoPE (dims 512 + 4 (lane % 16) ..) of token 4 wave + lane / 16.  A
+// wave thus dequantises 64 consecutive 16-byte chunks of one token per store
+// (conflict-free LDS writes) from 512 consecutive code bytes, and every wave
+// does the same loads and stores.
 struct RawFp8 {
   u32x2 v[4];
   float sc[4];
-  u32x4 r;
+  u32x2 r;
 };
 
 template <bool FP8, bool SPARSE>
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   MLA_LDS char* pbuf = smem + kPOffset;
   MLA_LDS int32_t* ring_idx = (MLA_LDS int32_t*)(smem + kMetaOffset);
-  MLA_LDS int32_t* ring_pg = ring_idx + kRing * 64;
+  MLA_LDS int32_t* ring_pg = ring_idx + kRingIdx * 64;
   MLA_LDS int32_t* wflag = (MLA_LDS int32_t*)(smem + kFlagOffset);
   MLA_LDS float* xrow = (MLA_LDS float*)(smem + kXOffset);
 
@@ -214,8 +216,13 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     const int seqlen = __builtin_amdgcn_readfirstlane(p.seqlens[b]);  // uniform: keeps what derives from it scalar
     const int32_t* bt_row = p.block_table + (int64_t)b * p.max_blocks;
     const int32_t* idx_row = SPARSE ? p.indices + (int64_t)stream * p.topk : nullptr;
+    // Buffer resources for the direct loads into LDS: MUBUF loads keep the
+    // compiler's wait counts exact (a FLAT load into LDS makes it drain every
+    // counter at each wait), and an offset past the range loads zeros.
     const __amdgpu_buffer_rsrc_t bt_rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)bt_row, 0, p.max_blocks * 4, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t idx_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)idx_row, 0, SPARSE ? p.topk * 4 : 0, kBufferFlags);
     // sub-tiles [u0, u1): 32 tokens (dense) or 32 index slots (sparse) each
     const int limit = SPARSE ? p.topk : seqlen;
     const int u0 = 2 * lo;
@@ -245,57 +252,60 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     // loads, waited for at the end of the next round; FP8: loads into VGPRs,
     // dequantised into LDS in the next round).  What a round needs to know about a
     // sub-tile (its cache page, or the index and page of each of its 32 slots) was
-    // fetched earlier by direct loads into LDS rings of 8 sub-tiles, issued by
-    // wave 0: round u fetches the page of sub-tile u + 5 (dense), or the indices of
-    // sub-tile u + 7 and the pages of sub-tile u + 5's indices (sparse); such a
+    // fetched earlier by direct loads into LDS rings (16 sub-tiles of indices, 8 of
+    // pages): round u fetches the page of sub-tile u + 6 (dense), or the indices
+    // of sub-tile u + 8 and the pages of sub-tile u + 6's indices (sparse); such a
     // load has landed and is visible two rounds later.  No loaded value ever lands
     // in a register it has to carry across rounds: the compiler could only wait
     // for it by draining every load still streaming.
     auto slot_ok = [&](int u) { return u < u1 && u * kSub + l32 < p.topk; };  // sparse slot l32 exists
+    // ring rows of sub-tile x
+    auto idx_slot = [&](int x) -> MLA_LDS int32_t* { return ring_idx + (x & (kRingIdx - 1)) * 64; };
+    auto pg_slot = [&](int x) -> MLA_LDS int32_t* { return ring_pg + (x & (kRingPg - 1)) * 64; };
     // Direct metadata loads into the rings (64 lanes each; lanes 32..63 repeat
     // 0..31): the indices of sub-tile x, the pages of sub-tile x's indices
     // (sparse; its indices must be visible), the page of sub-tile x (dense; the
     // split's last page past its end).
     auto fetch_idx = [&](int x) {
       const int si = min(x * kSub + l32, p.topk - 1);
-      global_load_lds4((const void*)(idx_row + si), (MLA_LDS void*)(ring_idx + (x & (kRing - 1)) * 64));
+      buffer_load_lds4(idx_rs, (MLA_LDS void*)idx_slot(x), (uint32_t)si * 4u);
     };
     auto fetch_pg = [&](int x) {
-      const int idx = ring_idx[(x & (kRing - 1)) * 64 + l32];
+      const int idx = idx_slot(x)[l32];
       const bool ok = slot_ok(x) && idx >= 0;
-      global_load_lds4((const void*)(bt_row + (ok ? idx >> 6 : 0)), (MLA_LDS void*)(ring_pg + (x & (kRing - 1)) * 64));
+      buffer_load_lds4(bt_rs, (MLA_LDS void*)pg_slot(x), (uint32_t)(ok ? idx >> 6 : 0) * 4u);
     };
     auto fetch_page = [&](int x) {
-      buffer_load_lds4(bt_rs, (MLA_LDS void*)(ring_pg + (x & (kRing - 1)) * 64), (uint32_t)(min(x, u1 - 1) >> 1) * 4u);
+      buffer_load_lds4(bt_rs, (MLA_LDS void*)pg_slot(x), (uint32_t)(min(x, u1 - 1) >> 1) * 4u);
     };
-    // round u's share: sparse part 0 the indices of sub-tile u + 7, part 1 the
-    // pages of sub-tile u + 5; dense the page of sub-tile u + 5
+    // round u's share: sparse part 0 the indices of sub-tile u + 8, part 1 the
+    // pages of sub-tile u + 6; dense the page of sub-tile u + 6
     auto meta_dma = [&](int u, int part) {
       if constexpr (SPARSE) {
         if (part == 0)
-          fetch_idx(u + 7);
+          fetch_idx(u + 8);
         else
-          fetch_pg(u + 5);
+          fetch_pg(u + 6);
       } else {
-        fetch_page(u + 5);
+        fetch_page(u + 6);
       }
     };
-    // prologue: the ring entries of sub-tiles u0 .. u0 + 4 (pages) and, sparse,
-    // u0 .. u0 + 6 (indices), one sub-tile per wave; ends with a barrier after
+    // prologue: the ring entries of sub-tiles u0 .. u0 + 5 (pages) and, sparse,
+    // u0 .. u0 + 7 (indices), one sub-tile per wave; ends with a barrier after
     // which they are visible
     auto meta_fill = [&]() {
       if constexpr (SPARSE) {
-        if (wave_s < 7) fetch_idx(u0 + wave_s);
+        fetch_idx(u0 + wave_s);
         tile_barrier_drain();
-        if (wave_s < 5) fetch_pg(u0 + wave_s);
+        if (wave_s < 6) fetch_pg(u0 + wave_s);
       } else {
-        if (wave_s < 5) fetch_page(u0 + wave_s);
+        if (wave_s < 6) fetch_page(u0 + wave_s);
       }
       tile_barrier_drain();
     };
     // attended mask of sub-tile u's 32 slots (sparse)
     auto sparse_mask = [&](int u) -> uint32_t {
-      const bool ok = slot_ok(u) && ring_idx[(u & (kRing - 1)) * 64 + l32] >= 0;
+      const bool ok = slot_ok(u) && idx_slot(u)[l32] >= 0;
       return (uint32_t)__ballot(ok);
     };
     // Dense visibility: the tokens [0, vis) a row attends.  Non-causal: the whole
@@ -348,13 +358,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     __amdgpu_buffer_rsrc_t st_rs;  // dense: the sub-tile's bytes inside the sequence
     int st_tok = -1;               // sparse: token row of slot l32
     auto stage_begin = [&](int u) {
-      const int r = (u & (kRing - 1)) * 64;
       if constexpr (SPARSE) {
-        const int idx = ring_idx[r + l32];
-        const int pg = ring_pg[r + l32];
+        const int idx = idx_slot(u)[l32];
+        const int pg = pg_slot(u)[l32];
         st_tok = (slot_ok(u) && idx >= 0) ? pg * kPage + (idx & 63) : -1;
       } else {
-        const int page = __builtin_amdgcn_readfirstlane(ring_pg[r]);
+        const int page = __builtin_amdgcn_readfirstlane(pg_slot(u)[0]);
         const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
         // tokens inside the sequence (scalar: the resource must be uniform)
         const int valid = __builtin_amdgcn_readfirstlane(min(max(seqlen - u * kSub, 0), kSub));
@@ -386,16 +395,21 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       if (wave_s < 4) stage_load(kLoads - 1, buf);
     };
     auto load_fp8 = [&](int u, RawFp8& r) {
-      const int rs = (u & (kRing - 1)) * 64;
       int lo = lane;
       asm volatile("" : "+v"(lo));  // per-lane offsets recomputed here, not kept live
-      const int tr = 8 * wave_s + (lo >> 3);  // waves 0..3: the token of this lane's RoPE chunk
+      const int tr = 4 * wave_s + (lo >> 4);  // the token of this lane's RoPE bytes
+      // the four tokens 8 k + wave are the same for the whole wave: their ring
+      // entries go to scalars, so their addresses are scalar arithmetic
       int ix[5], pg[5];
 #pragma unroll
       for (int k = 0; k < 5; ++k) {
         const int t = k < 4 ? 8 * k + wave_s : tr;
-        ix[k] = SPARSE ? ring_idx[rs + t] : 0;
-        pg[k] = ring_pg[SPARSE ? rs + t : rs];
+        ix[k] = SPARSE ? idx_slot(u)[t] : 0;
+        pg[k] = pg_slot(u)[SPARSE ? t : 0];
+        if (k < 4) {
+          ix[k] = __builtin_amdgcn_readfirstlane(ix[k]);
+          pg[k] = __builtin_amdgcn_readfirstlane(pg[k]);
+        }
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -403,7 +417,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         r.v[k] = *(const u32x2*)(pt + 8 * lo);
         r.sc[k] = *(const float*)(pt + kFp8Dims + 4 * (lo >> 4));
       }
-      if (wave_s < 4) r.r = *(const u32x4*)(token_ptr(u, tr, ix[4], pg[4]) + kFp8Dims + 16 + 16 * (lo & 7));
+      r.r = *(const u32x2*)(token_ptr(u, tr, ix[4], pg[4]) + kFp8Dims + 16 + 8 * (lo & 15));
     };
     // Token 8 k + wave's swizzle is 4 bit1(wave) + 2 (k & 1), so the store
     // address of chunk `lane` is one of two per-lane bases plus 8 k token rows.
@@ -417,7 +431,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         const u32x2 a = dequant4(r.v[k].x, r.sc[k]), b = dequant4(r.v[k].y, r.sc[k]);
         *(MLA_LDS u32x4*)(buf + ((k & 1) ? b1 : b0) + 8 * k * kBf16TokenBytes) = u32x4{a.x, a.y, b.x, b.y};
       }
-      if (wave_s < 4) *(MLA_LDS u32x4*)(buf + tile_slot(8 * wave_s + (lo >> 3), 64 + (lo & 7)) * 16) = r.r;
+      const int tr = 4 * wave_s + (lo >> 4);
+      *(MLA_LDS u32x2*)(buf + tile_slot(tr, 64 + ((lo & 15) >> 1)) * 16 + 8 * (lo & 1)) = r.r;
     };
     // ---- operand reads ------------------------------------------------------------
     auto kread = [&](MLA_LDS char* kb, int kk) -> bf16x8 {
