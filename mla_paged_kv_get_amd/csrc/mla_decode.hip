@@ -112,10 +112,10 @@ constexpr int kBufferFlags = 0x00020000;
 
 // FP8 registers of one sub-tile for this thread: for k = 0..3 the 8 codes of
 // dims 8 lane .. of token 8 k + wave and their scale (scale lane / 16), and 8
-// bytes of RoPE (dims 512 + 4 (lane % 16) ..) of token 4 wave + lane / 16.  A
+// bytes of RoPE (dims 512 + 4 (lane % 16) ..) of token 8 (lane / 16) + wave.  A
 // wave thus dequantises 64 consecutive 16-byte chunks of one token per store
-// (conflict-free LDS writes) from 512 consecutive code bytes, and every wave
-// does the same loads and stores.
+// (conflict-free LDS writes) from 512 consecutive code bytes, handles only its
+// own four tokens, and every wave does the same loads and stores.
 struct RawFp8 {
   u32x2 v[4];
   float sc[4];
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
   const int l16 = lane & 15, h4 = lane >> 4;  // 16x16 operand row / k-group
   const int l32 = lane & 31, h2 = lane >> 5;  // 32x32 operand row / k-group
   // scores: rows 16 r4 .., tokens 16 tb .. of each sub-tile
-  const int r4 = wave & 3, tb = wave >> 2;
+  const int r4 = wave_s & 3, tb = wave_s >> 2;  // scalars
   const int qrow = 16 * r4 + l16;  // this lane's query row (0..63) in the score and softmax steps
 
   // workgroup -> (worker, row tile); the row tiles of one worker share an XCD
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     const int tok = 8 * h2 + q;
     const int sw = tile_swizzle(tok);
     const int sb = sw >> 2;
-    const int base = tok * kBf16TokenBytes + 128 * wave + ((cl ^ (sw & 3)) << 4) + 8 * (lane & 1);
+    const int base = tok * kBf16TokenBytes + 128 * wave_s + ((cl ^ (sw & 3)) << 4) + 8 * (lane & 1);
     vofs[0] = base + 64 * sb;
     vofs[1] = base - 64 * sb;
   }
@@ -290,6 +290,47 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         fetch_page(u + 6);
       }
     };
+    // FP8 metadata goes through VGPRs instead (its tile loads are VGPR loads,
+    // two rounds in flight, and the compiler counts register loads exactly):
+    // every wave loads, in round u before that round's tile loads, the indices of
+    // sub-tile u + 8 and the pages of sub-tile u + 6 (dense: its page), and wave 0
+    // writes them into the rings in round u + 1, right after the store that waits
+    // for the tile loads issued before them, so the write costs no extra wait;
+    // they are visible from round u + 2 on, as with the direct loads.
+    struct Fp8Meta {
+      int idx, pg;
+    };
+    auto fp8_meta_load = [&](int u) -> Fp8Meta {
+      int z = 0;
+      asm volatile("" : "+v"(z));  // a per-lane index, so these are vector loads
+      Fp8Meta m;
+      if constexpr (SPARSE) {
+        m.idx = idx_row[min((u + 8) * kSub + l32, p.topk - 1) + z];
+        const int i6 = idx_slot(u + 6)[l32];
+        m.pg = bt_row[(slot_ok(u + 6) && i6 >= 0 ? i6 >> 6 : 0) + z];
+      } else {
+        m.idx = 0;
+        m.pg = bt_row[(min(u + 6, u1 - 1) >> 1) + z];
+      }
+      return m;
+    };
+    // FP8 sparse keeps, in place of each slot's page, the slot's token row
+    // (page * 64 + index % 64, or -1 when the slot is not attended), so a tile load
+    // costs one ring read and a multiply.
+    auto fp8_token_row = [&](int x, int pg) -> int {
+      const int i = idx_slot(x)[l32];
+      return slot_ok(x) && i >= 0 ? pg * kPage + (i & 63) : -1;
+    };
+    auto fp8_meta_publish = [&](int u, const Fp8Meta& m) {  // round u's loads, by wave 0
+      if (wave_s == 0) {
+        if constexpr (SPARSE) {
+          idx_slot(u + 8)[lane] = m.idx;
+          pg_slot(u + 6)[lane] = fp8_token_row(u + 6, m.pg);
+        } else {
+          pg_slot(u + 6)[lane] = m.pg;
+        }
+      }
+    };
     // prologue: the ring entries of sub-tiles u0 .. u0 + 5 (pages) and, sparse,
     // u0 .. u0 + 7 (indices), one sub-tile per wave; ends with a barrier after
     // which they are visible
@@ -305,7 +346,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     };
     // attended mask of sub-tile u's 32 slots (sparse)
     auto sparse_mask = [&](int u) -> uint32_t {
-      const bool ok = slot_ok(u) && idx_slot(u)[l32] >= 0;
+      const bool ok = FP8 ? pg_slot(u)[l32] >= 0 : slot_ok(u) && idx_slot(u)[l32] >= 0;
       return (uint32_t)__ballot(ok);
     };
     // Dense visibility: the tokens [0, vis) a row attends.  Non-causal: the whole
@@ -337,18 +378,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     };
     // ---- staging ------------------------------------------------------------------
     auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((unsigned)(u - u0) & (kNBuf - 1)) * kSubBytes; };
-    // FP8: byte address of stored token t of sub-tile u (the zero token when not
-    // attended), from its ring entries (sparse: idx, pg; dense: the page), which
-    // the caller reads first for all of its tokens, so their LDS latencies overlap.
-    auto token_ptr = [&](int u, int t, int idx, int pg) -> const uint8_t* {
-      if (SPARSE) {
-        const bool ok = u < u1 && u * kSub + t < p.topk && idx >= 0;
-        return ok ? p.kv + ((int64_t)pg * kPage + (idx & 63)) * tok_bytes : g_zero_token;
-      }
-      // past the split the ring slot may never have been written: its page is not used
-      if (u >= u1 || u * kSub + t >= seqlen) return g_zero_token;
-      return p.kv + ((int64_t)pg * kPage + (u & 1) * kSub + t) * tok_bytes;
-    };
     // BF16 direct loads of sub-tile u: this thread's five (or four) 16-byte
     // pieces.  Dense tiles use buffer loads against a resource that covers only
     // the sub-tile's tokens inside the sequence, so the pieces of tokens past
@@ -394,30 +423,46 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       for (int k = 0; k < kLoads - 1; ++k) stage_load(k, buf);
       if (wave_s < 4) stage_load(kLoads - 1, buf);
     };
+    // The four tokens 8 k + wave are the same for the whole wave, so their ring
+    // entries go to scalars and their addresses are scalar arithmetic; a token
+    // that is not attended (or lies past the sequence or the split) reads the
+    // zero token.
     auto load_fp8 = [&](int u, RawFp8& r) {
       int lo = lane;
       asm volatile("" : "+v"(lo));  // per-lane offsets recomputed here, not kept live
-      const int tr = 4 * wave_s + (lo >> 4);  // the token of this lane's RoPE bytes
-      // the four tokens 8 k + wave are the same for the whole wave: their ring
-      // entries go to scalars, so their addresses are scalar arithmetic
-      int ix[5], pg[5];
+      const uint8_t* pt[4];
+      if constexpr (SPARSE) {
+        int tk[4];
 #pragma unroll
-      for (int k = 0; k < 5; ++k) {
-        const int t = k < 4 ? 8 * k + wave_s : tr;
-        ix[k] = SPARSE ? idx_slot(u)[t] : 0;
-        pg[k] = pg_slot(u)[SPARSE ? t : 0];
-        if (k < 4) {
-          ix[k] = __builtin_amdgcn_readfirstlane(ix[k]);
-          pg[k] = __builtin_amdgcn_readfirstlane(pg[k]);
+        for (int k = 0; k < 4; ++k) tk[k] = pg_slot(u)[8 * k + wave_s];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          tk[k] = __builtin_amdgcn_readfirstlane(tk[k]);
+          pt[k] = u < u1 && tk[k] >= 0 ? p.kv + (int64_t)tk[k] * tok_bytes : g_zero_token;
+        }
+      } else {
+        // past the split the ring slot may never have been written: its page is not used
+        const int valid = u < u1 ? seqlen - u * kSub : 0;  // tokens of the sub-tile in the sequence
+        const int page = __builtin_amdgcn_readfirstlane(pg_slot(u)[0]);
+        const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * tok_bytes;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int t = 8 * k + wave_s;
+          pt[k] = t < valid ? base + t * tok_bytes : g_zero_token;
         }
       }
+      // unsigned lane offsets: the loads take the scalar token address plus a
+      // 32-bit per-lane offset
+      const uint32_t ul = (uint32_t)lo;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint8_t* pt = token_ptr(u, 8 * k + wave_s, ix[k], pg[k]);
-        r.v[k] = *(const u32x2*)(pt + 8 * lo);
-        r.sc[k] = *(const float*)(pt + kFp8Dims + 4 * (lo >> 4));
+        r.v[k] = *(const u32x2*)(pt[k] + 8u * ul);
+        r.sc[k] = *(const float*)(pt[k] + (uint32_t)kFp8Dims + 4u * (ul >> 4));
       }
-      r.r = *(const u32x2*)(token_ptr(u, tr, ix[4], pg[4]) + kFp8Dims + 16 + 8 * (lo & 15));
+      // RoPE bytes: lanes 16 k .. 16 k + 15 cover token 8 k + wave
+      const uint32_t kr = ul >> 4;
+      const uint8_t* prr = kr == 0 ? pt[0] : kr == 1 ? pt[1] : kr == 2 ? pt[2] : pt[3];
+      r.r = *(const u32x2*)(prr + (uint32_t)(kFp8Dims + 16) + 8u * (ul & 15u));
     };
     // Token 8 k + wave's swizzle is 4 bit1(wave) + 2 (k & 1), so the store
     // address of chunk `lane` is one of two per-lane bases plus 8 k token rows.
@@ -431,7 +476,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         const u32x2 a = dequant4(r.v[k].x, r.sc[k]), b = dequant4(r.v[k].y, r.sc[k]);
         *(MLA_LDS u32x4*)(buf + ((k & 1) ? b1 : b0) + 8 * k * kBf16TokenBytes) = u32x4{a.x, a.y, b.x, b.y};
       }
-      const int tr = 4 * wave_s + (lo >> 4);
+      const int tr = 8 * (lo >> 4) + wave_s;
       *(MLA_LDS u32x2*)(buf + tile_slot(tr, 64 + ((lo & 15) >> 1)) * 16 + 8 * (lo & 1)) = r.r;
     };
     // ---- operand reads ------------------------------------------------------------
@@ -467,26 +512,36 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     float m_ref = kNegInf, m_seen = kNegInf, l_sum = 0.f;
     bool redo = false;
     int pass = 0;  // at most two: the second pass runs with the split's row maximum
-    constexpr int kAhead = 4;   // K fragments read ahead of their score MFMA
-    constexpr int kPRead = 13;  // score MFMA after which the P fragments are read
+    constexpr int kAhead = FP8 ? (SPARSE ? 2 : 3) : 4;  // K fragments read ahead of their score MFMA
+    constexpr bool kPreK = !FP8;           // the first ones read before the round's barrier
+    constexpr int kPRead = FP8 ? 16 : 13;  // score MFMA after which the P fragments are read
     do {
       l_sum = 0.f;
       bool overflow = false;
 
       // ---- prologue ---------------------------------------------------------------
       // BF16: sub-tiles u0 .. u0 + 2 issued, u0 and u0 + 1 landed.  FP8: u0 and
-      // u0 + 1 stored, u0 + 2 in flight in VGPRs.  Then S of u0 and the reference.
-      RawFp8 raw;  // FP8: the next sub-tile to store, in VGPRs
+      // u0 + 1 stored, u0 + 2 and u0 + 3 in flight in VGPRs.  Then S of u0 and the
+      // reference.
+      RawFp8 raw[2];       // FP8: sub-tile x in VGPRs (set (x - u0) & 1) until its store
+      Fp8Meta fmeta[2];    // FP8: metadata loaded in a round of each set, written next round
       if constexpr (FP8) {
         meta_fill();
-        {
-          RawFp8 r1;
-          load_fp8(u0, raw);
-          load_fp8(u0 + 1, r1);
-          store_fp8(raw, buffer(u0));
-          store_fp8(r1, buffer(u0 + 1));
+        if constexpr (SPARSE) {
+          // the prologue's pages become token rows
+          if (wave_s < 6) {
+            const int x = u0 + wave_s;
+            const int tk = fp8_token_row(x, pg_slot(x)[l32]);
+            pg_slot(x)[lane] = tk;
+          }
+          lds_barrier();
         }
-        load_fp8(u0 + 2, raw);
+        load_fp8(u0, raw[0]);
+        load_fp8(u0 + 1, raw[1]);
+        store_fp8(raw[0], buffer(u0));
+        store_fp8(raw[1], buffer(u0 + 1));
+        load_fp8(u0 + 2, raw[0]);
+        load_fp8(u0 + 3, raw[1]);
         lds_barrier();
       } else {
         meta_fill();
@@ -558,10 +613,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       // BF16 load accounting: a round that stages issues exactly kLoads vector
       // memory operations per wave (waves 0..3 five tile pieces, waves 4..7 four
       // and one metadata load), so its closing wait is one count for every wave.
-      auto round = [&](auto first_tag, auto issue_tag, const int u, MLA_LDS char* __restrict__ kb,
+      auto round = [&](auto first_tag, auto issue_tag, auto set_tag, const int u, MLA_LDS char* __restrict__ kb,
                        MLA_LDS char* __restrict__ kn, MLA_LDS char* __restrict__ nxt) __attribute__((always_inline)) {
         constexpr bool kFirst = decltype(first_tag)::value != 0;
         constexpr int kIssue = decltype(issue_tag)::value;
+        constexpr int kSet = decltype(set_tag)::value;  // FP8: the VGPR set this round stores and refills
         const bool issue = kIssue == 1 || u + 3 < u1;  // sub-tile u + 3 exists (workgroup-uniform)
         __builtin_amdgcn_sched_barrier(0);
         // staging work placed after score MFMA kk
@@ -571,16 +627,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
             // (past the split they read in-bounds bytes that are never used), so
             // that the compiler's wait for them is a count on every path.
             if (kk == 1) {
-              store_fp8(raw, nxt);
-              // every load issued before this round (the metadata included) has
-              // landed; the round's barrier publishes it
-              asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+              store_fp8(raw[kSet], nxt);  // sub-tile u + 2, loaded two rounds ago
+              if (!kFirst) fp8_meta_publish(u - 1, fmeta[kSet ^ 1]);
             }
-            if (kk == 2 && wave_s == 0 && issue) {
-              meta_dma(u, 0);
-              if (SPARSE) meta_dma(u, 1);
-            }
-            if (kk == 3) load_fp8(u + 3, raw);
+            if (kk == 2) fmeta[kSet] = fp8_meta_load(u);
+            if (kk == 3) load_fp8(u + 4, raw[kSet]);
           } else {
             if (issue) {
               if (kk == 0) stage_begin(u + 3);
@@ -596,6 +647,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         };
         bf16x8 pp[2][2];  // P of sub-tile u - 1, read while the last score MFMAs run
         if constexpr (!kFirst) {
+          if constexpr (!kPreK)
+#pragma unroll
+            for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kb, kk);
           s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < 18; ++kk) {
@@ -648,10 +702,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
             if (s2 == 0 && ct == 0) softmax();
             __builtin_amdgcn_sched_barrier(0);
           }
-        // the first K fragments of sub-tile u + 1
-        if (kIssue == 1 || u + 1 < u1)
+        // the first K fragments of sub-tile u + 1 (BF16; FP8 spends these VGPRs on
+        // its second tile set and reads them after the barrier)
+        if constexpr (kPreK)
+          if (kIssue == 1 || u + 1 < u1)
 #pragma unroll
-          for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kn, kk);
+            for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kn, kk);
         if constexpr (FP8) {
           lds_barrier();  // sub-tile u + 2 went through registers
         } else if (issue) {
@@ -661,11 +717,20 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         }
       };
       constexpr int kStageAhead = FP8 ? 2 : 3;  // the sub-tile a round stages
-      round(Tag<1>{}, Tag<-1>{}, u0, buffer(u0), buffer(u0 + 1), buffer(u0 + kStageAhead));
+      round(Tag<1>{}, Tag<-1>{}, Tag<0>{}, u0, buffer(u0), buffer(u0 + 1), buffer(u0 + kStageAhead));
       int u = u0 + 1;
-      // main loop: every round stages an existing sub-tile; then the last rounds
-      for (; u + 3 < u1; ++u) round(Tag<0>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
-      for (; u < u1; ++u) round(Tag<0>{}, Tag<-1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+      if constexpr (FP8) {
+        // unrolled by two: round u stores and refills VGPR set (u - u0) & 1
+        for (; u + 1 < u1; u += 2) {
+          round(Tag<0>{}, Tag<-1>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+          round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, u + 1, buffer(u + 1), buffer(u + 2), buffer(u + 1 + kStageAhead));
+        }
+        if (u < u1) round(Tag<0>{}, Tag<-1>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+      } else {
+        // main loop: every round stages an existing sub-tile; then the last rounds
+        for (; u + 3 < u1; ++u) round(Tag<0>{}, Tag<1>{}, Tag<0>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+        for (; u < u1; ++u) round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+      }
 
       // PV of the last sub-tile
       {
@@ -686,7 +751,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       // the restart must be taken by the whole workgroup (it contains barriers);
       // the vote is over every lane, so it is taken before the lane-0 store
       const bool wave_overflow = __ballot(overflow) != 0;
-      if (lane == 0) wflag[wave] = wave_overflow ? 1 : 0;
+      if (lane == 0) wflag[wave_s] = wave_overflow ? 1 : 0;
       __syncthreads();
       redo = false;
 #pragma unroll
@@ -709,17 +774,23 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     // and the two token blocks; m_ref of each row from its score waves.
     l_sum += __shfl_xor(l_sum, 16);
     l_sum += __shfl_xor(l_sum, 32);
-    if (h4 == 0) {
-      xrow[tb * 64 + qrow] = l_sum;
-      if (tb == 0) xrow[128 + qrow] = m_ref;
+    {
+      int lo = lane;
+      asm volatile("" : "+v"(lo));  // the row index is formed here, not kept live across the loop
+      const int qr = 16 * r4 + (lo & 15);
+      if (lo < 16) {
+        xrow[tb * 64 + qr] = l_sum;
+        if (tb == 0) xrow[128 + qr] = m_ref;
+      }
     }
     __syncthreads();
     {
       // this lane's first output column; computed here (not hoisted out of the
       // stream loop, where it would hold registers the main loop needs)
-      int col = 64 * wave + 4 * h2;
-      int lrow = l32;
-      asm volatile("" : "+v"(col), "+v"(lrow));
+      int lo = lane;
+      asm volatile("" : "+v"(lo));
+      const int col = 64 * wave_s + 4 * (lo >> 5);
+      const int lrow = lo & 31;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const int rho = 32 * rb + lrow;  // row within the tile
@@ -745,7 +816,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
                 *(u32x2*)(orow + ct * 32 + 8 * i) =
                     u32x2{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1)};
               }
-            if (wave == 0 && h2 == 0) p.lse[row_base + rowj] = lse_v;
+            if (wave_s == 0 && h2 == 0) p.lse[row_base + rowj] = lse_v;
           } else {
             float* prow = p.part_o + ((int64_t)sid * p.R_stream + rowj) * kDV + col;
 #pragma unroll
@@ -756,7 +827,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
                 *(f32x4*)(prow + ct * 32 + 8 * i) =
                     f32x4{a[4 * i] * inv, a[4 * i + 1] * inv, a[4 * i + 2] * inv, a[4 * i + 3] * inv};
               }
-            if (wave == 0 && h2 == 0) p.part_lse[(int64_t)sid * p.R_stream + rowj] = lse_v;
+            if (wave_s == 0 && h2 == 0) p.part_lse[(int64_t)sid * p.R_stream + rowj] = lse_v;
           }
         }
       }
