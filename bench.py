@@ -55,13 +55,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mla_decode_kernel_dense_b
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads", default="2", help="comma list of configurations; 2 (the headline) is always run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--no-headline", action="store_true",
                     help="run only the --workloads listed (the first one is reported); for per-workload profiles")
+    ap.add_argument("--no-calls", action="store_true",
+                    help="skip the separate warm/cold call timings (for kernel traces of the timed steps alone)")
     return ap.parse_args()
 
 
@@ -100,7 +102,7 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 8}))
 
 
-def measure(cfg: int, steps: int, warmup: int):
+def measure(cfg: int, steps: int, warmup: int, calls: bool = True):
     import torch
 
     import mla_inputs as mi
@@ -170,8 +172,10 @@ def measure(cfg: int, steps: int, warmup: int):
         times.sort()
         return times[len(times) // 2]
 
-    call_warm = timed_calls(False)
-    call_cold = timed_calls(True)
+    # (skipped with --no-calls, so that a kernel trace of the run holds only the
+    # warmup and timed steps and its mean decode duration is the one reported)
+    call_warm = timed_calls(False) if calls else float("nan")
+    call_cold = timed_calls(True) if calls else float("nan")
     # the scheduler kernel alone
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     hold_gpu(100.0 * steps + 2000.0)
@@ -194,9 +198,12 @@ def measure(cfg: int, steps: int, warmup: int):
                kernel_gbps=round(nbytes / (kernel_ms * 1e-3) / 1e9, 1),
                call_cold_tflops=round(flops / (call_cold * 1e-3) / 1e12, 2),
                call_cold_gbps=round(nbytes / (call_cold * 1e-3) / 1e9, 1))
+    for k, v in list(res.items()):  # timings skipped with --no-calls
+        if isinstance(v, float) and v != v:
+            res[k] = None
     res["kernel_frac_hbm"] = round(res["kernel_gbps"] / PEAK_HBM_GBS, 4)
     res["kernel_frac_mfma"] = round(res["kernel_tflops"] / PEAK_BF16_TFLOPS, 4)
-    if topk == 0 and prob.s_q > 1:
+    if calls and topk == 0 and prob.s_q > 1:
         # speculative query tokens with the causal mask (query token s of s_q sees
         # positions <= seqlen - s_q + s): the same decode kernel, timed the same way
         ct = mla.DecodeKernelTimer()
@@ -254,10 +261,10 @@ def main():
     results = {}
     head_prob = None
     for c in cfgs:
-        prob, r = measure(c, args.steps, args.warmup)
+        prob, r = measure(c, args.steps, args.warmup, calls=not args.no_calls)
         results[c] = r
-        print("[bench] config %d %s: step %.1f us, decode kernel %.1f us (%.1f TFLOP/s, %.0f GB/s), call warm %.1f us, "
-              "cold %.1f us, scheduler %.1f us, W=%d, %d splits" % (
+        print("[bench] config %d %s: step %.1f us, decode kernel %.1f us (%.1f TFLOP/s, %.0f GB/s), call warm %s us, "
+              "cold %s us, scheduler %.1f us, W=%d, %d splits" % (
                   c, prob.name, r["step_us"], r["decode_kernel_us"], r["kernel_tflops"], r["kernel_gbps"],
                   r["decode_call_us_warm_median"], r["decode_call_us_cold_median"], r["scheduler_us"],
                   r["num_workers"], r["splits"]), file=sys.stderr, flush=True)
