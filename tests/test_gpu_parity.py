@@ -131,6 +131,18 @@ def test_forced_worker_counts(W):
     check_problem(sp, num_workers=W, what="sparse fp8 W=%d" % W)
 
 
+@pytest.mark.parametrize("is_fp8,topk", [(False, 0), (True, 0), (False, 320), (True, 320)],
+                         ids=["dense bf16", "dense fp8", "sparse bf16", "sparse fp8"])
+@pytest.mark.parametrize("W", [5, 19, 61, 150])
+def test_split_lengths_every_variant(is_fp8, topk, W):
+    """Worker counts that cut the streams into splits of one to several 32-token
+    sub-tiles (odd and even counts), for each kernel variant: the pipeline's
+    prologue, its main loop and its last rounds all see short and long splits."""
+    prob = mi.make_problem("splits", 3, 1, 64, [1500, 333, 770], seed=40 + W, topk=topk, is_fp8=is_fp8,
+                           n_invalid=7 if topk else 0, recipe="clip")
+    check_problem(prob, num_workers=W, what="%s topk=%d W=%d" % ("fp8" if is_fp8 else "bf16", topk, W))
+
+
 # --------------------------------------------------------------------------------------
 # edge cases
 
