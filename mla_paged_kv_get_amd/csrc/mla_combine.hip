@@ -9,7 +9,8 @@
 // (the same addresses for all 128 threads of a row, so one request per wave),
 // forms L and the weights itself, and issues its split outputs' loads eight
 // at a time, so a workgroup pays one memory round trip per eight splits instead
-// of one per row it visits.
+// of one per row it visits.  With at most sixteen splits the lse values and
+// the split outputs are loaded together: one round trip in all.
 #include "mla_common.hpp"
 
 namespace mla {
@@ -17,8 +18,12 @@ namespace mla {
 namespace {
 
 constexpr int kCombineThreads = 256;  // two rows x 128 threads (4 columns each)
-constexpr int kCombineBatch = 8;      // split outputs in flight per thread
+constexpr int kCombineBatch = 8;  // split outputs in flight per thread
 
+// kCombineFused: up to this many splits, the lse values and the outputs are
+// loaded together (8 or 16; the wider variant holds more VGPRs, so fewer waves
+// fit on a CU, and the host uses it only when streams have many splits).
+template <int kCombineFused>
 __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodeParams p) {
   const int stream = blockIdx.x;
   const int32_t* split_off = p.meta + meta_split_offset(p.W);
@@ -34,15 +39,61 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodePara
   const float* po = p.part_o + ((int64_t)s0 * p.R_stream + row) * kDV + c;
   const int64_t stride = (int64_t)p.R_stream * kDV;
 
-  // L = ln sum_j exp(lse_j), evaluated around the largest lse
+  auto write_out = [&](const float4& acc, float L) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 a, b;
+    a.x = (__bf16)acc.x;
+    a.y = (__bf16)acc.y;
+    b.x = (__bf16)acc.z;
+    b.y = (__bf16)acc.w;
+    *(uint2*)(p.o + (row_base + row) * kDV + c) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+    if (c == 0) p.lse[row_base + row] = L;
+  };
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  if (n <= kCombineFused) {
+    // Every split's output is loaded together with the lse values, before its
+    // weight is known.  L = ln sum_j exp(lse_j), evaluated around the largest
+    // lse; a split with lse = -inf (empty) has weight 0 and its output is not
+    // used.
+    float lj[kCombineFused];
+    float4 v[kCombineFused];
+#pragma unroll
+    for (int k = 0; k < kCombineFused; ++k) {
+      lj[k] = k < n ? lse_col[(int64_t)k * p.R_stream] : kNegInf;
+      v[k] = k < n ? *(const float4*)(po + k * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int k = 0; k < kCombineFused; ++k) mx = fmaxf(mx, lj[k]);
+    if (mx == kNegInf) {
+      write_out(acc, kNegInf);
+      return;
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < kCombineFused; ++k) sum += lj[k] == kNegInf ? 0.f : __expf(lj[k] - mx);
+    const float L = mx + __logf(sum);
+#pragma unroll
+    for (int k = 0; k < kCombineFused; ++k) {
+      if (lj[k] == kNegInf) continue;
+      const float w = __expf(lj[k] - L);
+      acc.x += w * v[k].x;
+      acc.y += w * v[k].y;
+      acc.z += w * v[k].z;
+      acc.w += w * v[k].w;
+    }
+    write_out(acc, L);
+    return;
+  }
+
+  // more splits: L first (the lse values), then the outputs eight at a time
   float mx = kNegInf;
   for (int j = 0; j < n; ++j) mx = fmaxf(mx, lse_col[(int64_t)j * p.R_stream]);
   float sum = 0.f;
   if (mx != kNegInf)
     for (int j = 0; j < n; ++j) sum += __expf(lse_col[(int64_t)j * p.R_stream] - mx);
   const float L = mx == kNegInf ? kNegInf : mx + __logf(sum);
-
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (L != kNegInf) {
     for (int j0 = 0; j0 < n; j0 += kCombineBatch) {
       float4 v[kCombineBatch];
@@ -64,21 +115,18 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodePara
       }
     }
   }
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 a, b;
-  a.x = (__bf16)acc.x;
-  a.y = (__bf16)acc.y;
-  b.x = (__bf16)acc.z;
-  b.y = (__bf16)acc.w;
-  *(uint2*)(p.o + (row_base + row) * kDV + c) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
-  if (c == 0) p.lse[row_base + row] = L;
+  write_out(acc, L);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.n_streams, (p.R_stream + 1) / 2);
-  hipLaunchKernelGGL(mla_combine_kernel, grid, dim3(kCombineThreads), 0, stream, p);
+  // more than 8 workers per stream: streams are likely cut into more than 8 splits
+  if (p.W > 8 * p.n_streams)
+    hipLaunchKernelGGL(mla_combine_kernel<16>, grid, dim3(kCombineThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(mla_combine_kernel<8>, grid, dim3(kCombineThreads), 0, stream, p);
   return hipGetLastError();
 }
 

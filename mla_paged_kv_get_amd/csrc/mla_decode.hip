@@ -547,9 +547,17 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         meta_fill();
         stage_bf16(u0, buffer(u0));
         if (u0 + 1 < u1) stage_bf16(u0 + 1, buffer(u0 + 1));
-        if (u0 + 2 < u1) {
-          stage_bf16(u0 + 2, buffer(u0 + 2));
-          // sub-tiles u0 and u0 + 1 landed; u0 + 2 (5 or 4 loads) stays in flight
+        if (u0 + 2 < u1) stage_bf16(u0 + 2, buffer(u0 + 2));
+        // only sub-tile u0 is waited for: the first scores need nothing else, and
+        // the loads of u0 + 1 and u0 + 2 (5 or 4 per wave each) stay in flight
+        // until the first round's closing wait
+        const int n_after = min(u1 - u0 - 1, 2);
+        if (n_after == 2) {
+          if (wave_s < 4)
+            barrier_keep<2 * kLoads>();
+          else
+            barrier_keep<2 * (kLoads - 1)>();
+        } else if (n_after == 1) {
           if (wave_s < 4)
             barrier_keep<kLoads>();
           else
@@ -613,9 +621,13 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       // BF16 load accounting: a round that stages issues exactly kLoads vector
       // memory operations per wave (waves 0..3 five tile pieces, waves 4..7 four
       // and one metadata load), so its closing wait is one count for every wave.
-      auto round = [&](auto first_tag, auto issue_tag, auto set_tag, const int u, MLA_LDS char* __restrict__ kb,
-                       MLA_LDS char* __restrict__ kn, MLA_LDS char* __restrict__ nxt) __attribute__((always_inline)) {
+      auto round = [&](auto first_tag, auto issue_tag, auto set_tag, auto kself_tag, const int u,
+                       MLA_LDS char* __restrict__ kb, MLA_LDS char* __restrict__ kn,
+                       MLA_LDS char* __restrict__ nxt) __attribute__((always_inline)) {
         constexpr bool kFirst = decltype(first_tag)::value != 0;
+        // this round reads its first K fragments itself (FP8 always; BF16 in the
+        // round after u0, whose sub-tile was still landing when round u0 ended)
+        constexpr bool kSelfK = decltype(kself_tag)::value != 0;
         constexpr int kIssue = decltype(issue_tag)::value;
         constexpr int kSet = decltype(set_tag)::value;  // FP8: the VGPR set this round stores and refills
         const bool issue = kIssue == 1 || u + 3 < u1;  // sub-tile u + 3 exists (workgroup-uniform)
@@ -647,7 +659,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         };
         bf16x8 pp[2][2];  // P of sub-tile u - 1, read while the last score MFMAs run
         if constexpr (!kFirst) {
-          if constexpr (!kPreK)
+          if constexpr (kSelfK)
 #pragma unroll
             for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kb, kk);
           s = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -704,7 +716,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
           }
         // the first K fragments of sub-tile u + 1 (BF16; FP8 spends these VGPRs on
         // its second tile set and reads them after the barrier)
-        if constexpr (kPreK)
+        if constexpr (kPreK && !kFirst)
           if (kIssue == 1 || u + 1 < u1)
 #pragma unroll
             for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kn, kk);
@@ -717,19 +729,26 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         }
       };
       constexpr int kStageAhead = FP8 ? 2 : 3;  // the sub-tile a round stages
-      round(Tag<1>{}, Tag<-1>{}, Tag<0>{}, u0, buffer(u0), buffer(u0 + 1), buffer(u0 + kStageAhead));
+      round(Tag<1>{}, Tag<-1>{}, Tag<0>{}, Tag<0>{}, u0, buffer(u0), buffer(u0 + 1), buffer(u0 + kStageAhead));
       int u = u0 + 1;
       if constexpr (FP8) {
         // unrolled by two: round u stores and refills VGPR set (u - u0) & 1
         for (; u + 1 < u1; u += 2) {
-          round(Tag<0>{}, Tag<-1>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
-          round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, u + 1, buffer(u + 1), buffer(u + 2), buffer(u + 1 + kStageAhead));
+          round(Tag<0>{}, Tag<-1>{}, Tag<1>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+          round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, Tag<1>{}, u + 1, buffer(u + 1), buffer(u + 2),
+                buffer(u + 1 + kStageAhead));
         }
-        if (u < u1) round(Tag<0>{}, Tag<-1>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+        if (u < u1) round(Tag<0>{}, Tag<-1>{}, Tag<1>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
       } else {
+        if (u < u1) {
+          round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+          ++u;
+        }
         // main loop: every round stages an existing sub-tile; then the last rounds
-        for (; u + 3 < u1; ++u) round(Tag<0>{}, Tag<1>{}, Tag<0>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
-        for (; u < u1; ++u) round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+        for (; u + 3 < u1; ++u)
+          round(Tag<0>{}, Tag<1>{}, Tag<0>{}, Tag<0>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+        for (; u < u1; ++u)
+          round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, Tag<0>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
       }
 
       // PV of the last sub-tile
