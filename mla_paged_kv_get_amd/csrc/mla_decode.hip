@@ -77,6 +77,18 @@ template <int N>
 __device__ __forceinline__ void barrier_keep() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+// The same through the builtin, whose wait the compiler's wait-count pass sees:
+// afterwards it knows the older loads (direct loads into LDS included) are
+// done and adds no waits of its own for them.  gfx9 s_waitcnt immediate:
+// vmcnt in bits 3:0 and 15:14, expcnt in 6:4 (7: no wait), lgkmcnt in 11:8.
+template <int N>
+__device__ __forceinline__ void barrier_keep_seen() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int V>
 struct Tag {
@@ -106,6 +118,7 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 // 512 k + tid (k < 4) and, for tid < 256, 2048 + tid.
 constexpr int kSlots = kSubBytes / 16;
 constexpr int kLoads = 5;
+constexpr int kFp8Loads = 9;  // vector memory operations of one FP8 sub-tile load (4 codes, 4 scales, RoPE)
 static_assert(kSlots == 4 * kDecThreads + kDecThreads / 2, "staging split");
 // Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle.
 constexpr int kBufferFlags = 0x00020000;
@@ -229,20 +242,41 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     const int u1 = min(2 * hi, (limit + kSub - 1) / kSub);
 
     // Q fragments (B operand of the score MFMA): row qrow, dims 32 kk + 8 h4 ..
+    // The row tile's 64 Q rows (contiguous, 1152 B each) are brought into two
+    // tile buffers by direct loads in the tile layout (rows in place of tokens,
+    // the same swizzle): one copy per workgroup in whole 1 KB runs, where
+    // per-lane register loads would fetch every row twice (both token-block
+    // waves of a row block) in 64-byte pieces.  Each wave then reads its 16 rows
+    // the way it reads K.  Rows past the stream's last load as zeros: the
+    // resource covers only existing rows.
     bf16x8 qf[18];
-    {
-      int lo = lane;
-      asm volatile("" : "+v"(lo));  // the row pointer is formed here, not kept live across pieces
-      const int row = rt * kRowTile + 16 * r4 + (lo & 15);
-      const bool row_ok = row < p.R_stream;
-      const uint16_t* qr = p.q + (row_base + (row_ok ? row : 0)) * kDQK + 8 * (lo >> 4);
+    auto stage_q = [&](int h, MLA_LDS char* buf) {  // rows 32 h .. 32 h + 31 of the tile
+      const int r0 = rt * kRowTile + 32 * h;
+      const int nrows = __builtin_amdgcn_readfirstlane(min(max(p.R_stream - r0, 0), 32));
+      const __amdgpu_buffer_rsrc_t q_rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.q + (row_base + r0) * kDQK), 0, nrows * kBf16TokenBytes, kBufferFlags);
+      int to = tid;
+      asm volatile("" : "+v"(to));  // slot offsets computed here, not kept live across the loop
 #pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
-        u32x4 v = *(const u32x4*)(qr + 32 * kk);
-        if (!row_ok) v = u32x4{0, 0, 0, 0};
-        qf[kk] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
+      for (int k = 0; k < kLoads; ++k)
+        if (k < kLoads - 1 || wave_s < 4) {
+          const int sl = min(k * kDecThreads + to, kSlots - 1);
+          const int t = sl / kTokenChunks;
+          buffer_load_lds16(q_rs, (MLA_LDS void*)(buf + k * (kDecThreads * 16) + wave_s * 1024),
+                            (uint32_t)(t * kBf16TokenBytes + ((sl - t * kTokenChunks) ^ tile_swizzle(t)) * 16));
+        }
+    };
+    auto read_q = [&](MLA_LDS char* b0, MLA_LDS char* b1) {  // rows 0..31 in b0, 32..63 in b1
+      int lo = lane;
+      asm volatile("" : "+v"(lo));  // recomputed here, not kept live across the loop
+      const int t = 16 * (r4 & 1) + (lo & 15);
+      const int sw = tile_swizzle(t);
+      MLA_LDS char* qb = (r4 >> 1) ? b1 : b0;
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk)
+        qf[kk] = *(MLA_LDS bf16x8*)(qb + t * kBf16TokenBytes + (((4 * (kk & 1) + (lo >> 4)) ^ sw) << 4) +
+                                    (kk >> 1) * 128);
+    };
 
     // O^T accumulators: [row block][32-column block], columns 64 wave + 32 ct ..
     f32x16 acc[2][2];
@@ -520,9 +554,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       bool overflow = false;
 
       // ---- prologue ---------------------------------------------------------------
-      // BF16: sub-tiles u0 .. u0 + 2 issued, u0 and u0 + 1 landed.  FP8: u0 and
-      // u0 + 1 stored, u0 + 2 and u0 + 3 in flight in VGPRs.  Then S of u0 and the
-      // reference.
+      // Q goes through the buffers of sub-tiles u0 + 2 and u0 + 3 before they
+      // hold tiles.  BF16: sub-tiles u0 and u0 + 1 and Q issued; u0 and Q landed;
+      // Q read; then u0 + 2 issued into its buffer.  FP8: u0 and u0 + 1 loaded and
+      // stored, Q landed and read, u0 + 2 and u0 + 3 in flight in VGPRs.  Then S
+      // of u0 and the reference, whose barrier ends every wave's reads of Q
+      // before round u0 stores sub-tile u0 + 2 there.
       RawFp8 raw[2];       // FP8: sub-tile x in VGPRs (set (x - u0) & 1) until its store
       Fp8Meta fmeta[2];    // FP8: metadata loaded in a round of each set, written next round
       if constexpr (FP8) {
@@ -538,33 +575,34 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         }
         load_fp8(u0, raw[0]);
         load_fp8(u0 + 1, raw[1]);
+        stage_q(0, buffer(u0 + 2));
+        stage_q(1, buffer(u0 + 3));
         store_fp8(raw[0], buffer(u0));
         store_fp8(raw[1], buffer(u0 + 1));
         load_fp8(u0 + 2, raw[0]);
         load_fp8(u0 + 3, raw[1]);
-        lds_barrier();
+        // Q's direct loads are older than the 2 x 9 register loads just issued
+        barrier_keep_seen<2 * kFp8Loads>();
+        read_q(buffer(u0 + 2), buffer(u0 + 3));
       } else {
         meta_fill();
+        // Sub-tile u0 + 1 is loaded even when the split ends first (the dense
+        // resource and the sparse zero token keep such loads in bounds; the
+        // buffer is not read), so every path issues the same loads.
         stage_bf16(u0, buffer(u0));
-        if (u0 + 1 < u1) stage_bf16(u0 + 1, buffer(u0 + 1));
-        if (u0 + 2 < u1) stage_bf16(u0 + 2, buffer(u0 + 2));
-        // only sub-tile u0 is waited for: the first scores need nothing else, and
-        // the loads of u0 + 1 and u0 + 2 (5 or 4 per wave each) stay in flight
-        // until the first round's closing wait
-        const int n_after = min(u1 - u0 - 1, 2);
-        if (n_after == 2) {
-          if (wave_s < 4)
-            barrier_keep<2 * kLoads>();
-          else
-            barrier_keep<2 * (kLoads - 1)>();
-        } else if (n_after == 1) {
-          if (wave_s < 4)
-            barrier_keep<kLoads>();
-          else
-            barrier_keep<kLoads - 1>();
-        } else {
-          tile_barrier_drain();
-        }
+        stage_q(0, buffer(u0 + 2));
+        stage_q(1, buffer(u0 + 3));
+        stage_bf16(u0 + 1, buffer(u0 + 1));
+        // u0 and Q landed; u0 + 1 (5 or 4 loads per wave) stays in flight
+        if (wave_s < 4)
+          barrier_keep<kLoads>();
+        else
+          barrier_keep<kLoads - 1>();
+        read_q(buffer(u0 + 2), buffer(u0 + 3));
+        lds_barrier();  // every wave has read Q before sub-tile u0 + 2 lands there
+        // (loaded whether or not it exists, as u0 + 1; waited for with u0 + 1 at
+        // the first round's closing wait)
+        stage_bf16(u0 + 2, buffer(u0 + 2));
       }
       // K fragments kk .. kk + kAhead - 1 of the next score step (rolling)
       bf16x8 kf[kAhead];
@@ -591,6 +629,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         const float m0 = fmaxf(xrow[qrow], xrow[64 + qrow]) * p.scale_log2;
         m_ref = m0 == kNegInf ? kNegInf : m0 + kRefLift;
         // xrow is next written after the loop, behind at least one round's barrier
+      } else if constexpr (FP8) {
+        // (the reference's barrier is what otherwise separates the reads of Q
+        // from round u0's store into the same buffer)
+        lds_barrier();
       }
 
       // (zeroed here, after the prologue's loads, not before them)
