@@ -118,6 +118,11 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 // 512 k + tid (k < 4) and, for tid < 256, 2048 + tid.
 constexpr int kSlots = kSubBytes / 16;
 constexpr int kLoads = 5;
+// epilogue staging of the output tile in the tile buffers: row strides of the
+// bf16 output and the fp32 partial output, padded by 16 bytes
+constexpr int kOutRowBf16 = kDV * 2 + 16;
+constexpr int kOutRowF32 = kDV * 4 + 16;
+static_assert(kRowTile * kOutRowF32 <= kNBuf * kSubBytes, "output staging fits the tile buffers");
 constexpr int kFp8Loads = 9;  // vector memory operations of one FP8 sub-tile load (4 codes, 4 scales, RoPE)
 static_assert(kSlots == 4 * kDecThreads + kDecThreads / 2, "staging split");
 // Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle.
@@ -845,6 +850,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       }
     }
     __syncthreads();
+    // The normalised rows go through LDS (the free tile buffers, rows padded by
+    // 16 bytes against bank conflicts) so that the global stores are whole
+    // contiguous runs: the tile's rows are contiguous in o and in the split's
+    // partial output, while each lane's accumulators hold 4 columns of 32
+    // different rows (per-lane stores would write 32 scattered pieces each).
+    const int nrows = min(p.R_stream - rt * kRowTile, kRowTile);  // rows of this tile that exist
     {
       // this lane's first output column; computed here (not hoisted out of the
       // stream loop, where it would hold registers the main loop needs)
@@ -861,39 +872,61 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         const bool empty = !(lj > 0.f);
         const float inv = empty ? 0.f : 1.f / lj;
         const float lse_v = empty ? kNegInf : (mj + __log2f(lj)) * 0.69314718055994531f;
-        if (rowj < p.R_stream) {
-          if (final_out) {
-            uint16_t* orow = p.o + (row_base + rowj) * kDV + col;
+        if (final_out) {
+          MLA_LDS char* orow = smem + rho * kOutRowBf16 + col * 2;
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+          for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const f32x16& a = acc[rb][ct];
-                bf16x2 v0, v1;
-                v0.x = (__bf16)(a[4 * i + 0] * inv);
-                v0.y = (__bf16)(a[4 * i + 1] * inv);
-                v1.x = (__bf16)(a[4 * i + 2] * inv);
-                v1.y = (__bf16)(a[4 * i + 3] * inv);
-                *(u32x2*)(orow + ct * 32 + 8 * i) =
-                    u32x2{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1)};
-              }
-            if (wave_s == 0 && h2 == 0) p.lse[row_base + rowj] = lse_v;
-          } else {
-            float* prow = p.part_o + ((int64_t)sid * p.R_stream + rowj) * kDV + col;
+            for (int i = 0; i < 4; ++i) {
+              const f32x16& a = acc[rb][ct];
+              bf16x2 v0, v1;
+              v0.x = (__bf16)(a[4 * i + 0] * inv);
+              v0.y = (__bf16)(a[4 * i + 1] * inv);
+              v1.x = (__bf16)(a[4 * i + 2] * inv);
+              v1.y = (__bf16)(a[4 * i + 3] * inv);
+              *(MLA_LDS u32x2*)(orow + (ct * 32 + 8 * i) * 2) =
+                  u32x2{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1)};
+            }
+          if (wave_s == 0 && h2 == 0 && rowj < p.R_stream) p.lse[row_base + rowj] = lse_v;
+        } else {
+          MLA_LDS char* prow = smem + rho * kOutRowF32 + col * 4;
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+          for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const f32x16& a = acc[rb][ct];
-                *(f32x4*)(prow + ct * 32 + 8 * i) =
-                    f32x4{a[4 * i] * inv, a[4 * i + 1] * inv, a[4 * i + 2] * inv, a[4 * i + 3] * inv};
-              }
-            if (wave_s == 0 && h2 == 0) p.part_lse[(int64_t)sid * p.R_stream + rowj] = lse_v;
-          }
+            for (int i = 0; i < 4; ++i) {
+              const f32x16& a = acc[rb][ct];
+              *(MLA_LDS f32x4*)(prow + (ct * 32 + 8 * i) * 4) =
+                  f32x4{a[4 * i] * inv, a[4 * i + 1] * inv, a[4 * i + 2] * inv, a[4 * i + 3] * inv};
+            }
+          if (wave_s == 0 && h2 == 0 && rowj < p.R_stream) p.part_lse[(int64_t)sid * p.R_stream + rowj] = lse_v;
         }
       }
     }
-    __syncthreads();  // LDS is reused by the next piece
+    lds_barrier();
+    {
+      // 16-byte chunk c of the tile: row c / (chunks per row); each wave stores 1 KB runs
+      int to = tid;
+      asm volatile("" : "+v"(to));
+      if (final_out) {
+        char* dst = (char*)(p.o + (row_base + rt * kRowTile) * kDV);
+#pragma unroll
+        for (int k = 0; k < kRowTile * kDV * 2 / 16 / kDecThreads; ++k) {
+          const int c = k * kDecThreads + to;
+          const int row = c >> 6, off = (c & 63) * 16;
+          if (row < nrows) *(u32x4*)(dst + row * (kDV * 2) + off) = *(MLA_LDS u32x4*)(smem + row * kOutRowBf16 + off);
+        }
+      } else {
+        char* dst = (char*)(p.part_o + ((int64_t)sid * p.R_stream + rt * kRowTile) * kDV);
+#pragma unroll
+        for (int k = 0; k < kRowTile * kDV * 4 / 16 / kDecThreads; ++k) {
+          const int c = k * kDecThreads + to;
+          const int row = c >> 7, off = (c & 127) * 16;
+          if (row < nrows) *(u32x4*)(dst + row * (kDV * 4) + off) = *(MLA_LDS u32x4*)(smem + row * kOutRowF32 + off);
+        }
+      }
+    }
+    // the next piece reuses LDS; after the last one there is nothing to wait for
+    if (stream < es && stream + 1 < p.n_streams) __syncthreads();
   }
 }
 
