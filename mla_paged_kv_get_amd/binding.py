@@ -206,13 +206,18 @@ class DecodeKernelTimer:
     mla_set_decode_kernel_events, runs fn() (which must make exactly one
     mla_decode_with_kvcache call on this thread) and clears the hook;
     `durations_ms()` synchronises and returns one duration per recorded call.
-    The events come from the HIP runtime the library itself is bound to.
+    The events come from the HIP runtime the library itself is bound to and
+    are created without the system-scope fence (hipEventDisableSystemFence):
+    they only time, and a default event's cache write-back and invalidation
+    between the kernels of a step would slow the very work being timed.
     """
+
+    _DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
 
     def __init__(self):
         lib()  # torch's HIP runtime is loaded and shared with the library by now
         self._hip = ctypes.CDLL("libamdhip64.so.7")
-        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
@@ -220,8 +225,8 @@ class DecodeKernelTimer:
 
     def _event(self):
         ev = ctypes.c_void_p()
-        if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
-            raise MlaError("hipEventCreate failed")
+        if self._hip.hipEventCreateWithFlags(ctypes.byref(ev), self._DISABLE_SYSTEM_FENCE) != 0:
+            raise MlaError("hipEventCreateWithFlags failed")
         return ev
 
     def record(self, fn):
