@@ -5,8 +5,8 @@
 // Streams with a single split were finished by the decode kernel; streams with
 // no tiles (seqlen 0) get o = 0 and lse = -inf.
 //
-// One thread per (query row, 4 columns): it reads the row's split lse values
-// (the same addresses for all 128 threads of a row, so one request per wave),
+// One thread per (query row, 8 columns): it reads the row's split lse values
+// (the same addresses for all 64 threads of a row, so one request per wave),
 // forms L and the weights itself, and issues its split outputs' loads eight
 // at a time, so a workgroup pays one memory round trip per eight splits instead
 // of one per row it visits.  With at most sixteen splits the lse values and
@@ -17,7 +17,7 @@ namespace mla {
 
 namespace {
 
-constexpr int kCombineThreads = 256;  // two rows x 128 threads (4 columns each)
+constexpr int kCombineThreads = 256;  // four rows x 64 threads (8 columns each)
 constexpr int kCombineBatch = 8;  // split outputs in flight per thread
 
 // kCombineFused: up to this many splits, the lse values and the outputs are
@@ -30,26 +30,32 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodePara
   const int s0 = split_off[stream];
   const int n = split_off[stream + 1] - s0;
   if (n == 1) return;  // finished by the decode kernel
-  const int row = blockIdx.y * 2 + (threadIdx.x >> 7);
+  const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (row >= p.R_stream) return;
-  const int c = (threadIdx.x & 127) * 4;
+  const int c = (threadIdx.x & 63) * 8;
   const int64_t row_base = (int64_t)stream * p.R_stream;
   constexpr float kNegInf = -__builtin_huge_valf();
   const float* lse_col = p.part_lse + (int64_t)s0 * p.R_stream + row;  // split j at j * R_stream
   const float* po = p.part_o + ((int64_t)s0 * p.R_stream + row) * kDV + c;
   const int64_t stride = (int64_t)p.R_stream * kDV;
 
-  auto write_out = [&](const float4& acc, float L) {
+  auto write_out = [&](const float4& acc, const float4& acc2, float L) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    bf16x2 a, b;
+    bf16x2 a, b, d, e;
     a.x = (__bf16)acc.x;
     a.y = (__bf16)acc.y;
     b.x = (__bf16)acc.z;
     b.y = (__bf16)acc.w;
-    *(uint2*)(p.o + (row_base + row) * kDV + c) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+    d.x = (__bf16)acc2.x;
+    d.y = (__bf16)acc2.y;
+    e.x = (__bf16)acc2.z;
+    e.y = (__bf16)acc2.w;
+    *(uint4*)(p.o + (row_base + row) * kDV + c) =
+        make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, d),
+                   __builtin_bit_cast(uint32_t, e));
     if (c == 0) p.lse[row_base + row] = L;
   };
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f), acc2 = acc;
 
   if (n <= kCombineFused) {
     // Every split's output is loaded together with the lse values, before its
@@ -57,17 +63,18 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodePara
     // lse; a split with lse = -inf (empty) has weight 0 and its output is not
     // used.
     float lj[kCombineFused];
-    float4 v[kCombineFused];
+    float4 v[kCombineFused], v2[kCombineFused];
 #pragma unroll
     for (int k = 0; k < kCombineFused; ++k) {
       lj[k] = k < n ? lse_col[(int64_t)k * p.R_stream] : kNegInf;
       v[k] = k < n ? *(const float4*)(po + k * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v2[k] = k < n ? *(const float4*)(po + k * stride + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float mx = kNegInf;
 #pragma unroll
     for (int k = 0; k < kCombineFused; ++k) mx = fmaxf(mx, lj[k]);
     if (mx == kNegInf) {
-      write_out(acc, kNegInf);
+      write_out(acc, acc2, kNegInf);
       return;
     }
     float sum = 0.f;
@@ -82,8 +89,12 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodePara
       acc.y += w * v[k].y;
       acc.z += w * v[k].z;
       acc.w += w * v[k].w;
+      acc2.x += w * v2[k].x;
+      acc2.y += w * v2[k].y;
+      acc2.z += w * v2[k].z;
+      acc2.w += w * v2[k].w;
     }
-    write_out(acc, L);
+    write_out(acc, acc2, L);
     return;
   }
 
@@ -96,7 +107,7 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodePara
   const float L = mx == kNegInf ? kNegInf : mx + __logf(sum);
   if (L != kNegInf) {
     for (int j0 = 0; j0 < n; j0 += kCombineBatch) {
-      float4 v[kCombineBatch];
+      float4 v[kCombineBatch], v2[kCombineBatch];
       float w[kCombineBatch];
 #pragma unroll
       for (int k = 0; k < kCombineBatch; ++k) {
@@ -105,6 +116,7 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodePara
         // an empty split (lse = -inf) carries weight 0 and its output is not read
         w[k] = lj == kNegInf ? 0.f : __expf(lj - L);
         v[k] = w[k] != 0.f ? *(const float4*)(po + j * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v2[k] = w[k] != 0.f ? *(const float4*)(po + j * stride + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int k = 0; k < kCombineBatch; ++k) {
@@ -112,16 +124,20 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodePara
         acc.y += w[k] * v[k].y;
         acc.z += w[k] * v[k].z;
         acc.w += w[k] * v[k].w;
+        acc2.x += w[k] * v2[k].x;
+        acc2.y += w[k] * v2[k].y;
+        acc2.z += w[k] * v2[k].z;
+        acc2.w += w[k] * v2[k].w;
       }
     }
   }
-  write_out(acc, L);
+  write_out(acc, acc2, L);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.n_streams, (p.R_stream + 1) / 2);
+  const dim3 grid(p.n_streams, (p.R_stream + 3) / 4);
   // more than 8 workers per stream: streams are likely cut into more than 8 splits
   if (p.W > 8 * p.n_streams)
     hipLaunchKernelGGL(mla_combine_kernel<16>, grid, dim3(kCombineThreads), 0, stream, p);
