@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t*
                                                                   int h_q, int topk, int W, int min_tiles,
                                                                   int32_t* __restrict__ meta) {
   __shared__ int64_t wave_sums[kSchedThreads / 64];
-  __shared__ int32_t lds_first[kLdsStreams + 1], lds_split[kLdsStreams + 1];
+  __shared__ int32_t lds_first[kLdsStreams + 1], lds_split[kLdsStreams + 1], lds_tiles[kLdsStreams];
   const int tid = threadIdx.x;
   const int n = topk > 0 ? B * s_q : B;
   int32_t* sched = meta + kMetaHeader;
@@ -83,14 +83,21 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t*
   const int per = (n + kSchedThreads - 1) / kSchedThreads;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
 
+  // each stream's tile count, read from memory once (kept in LDS when it fits)
+  auto tiles_of = [&](int i) -> int64_t { return in_lds ? (int64_t)lds_tiles[i] : stream_tiles(seqlens, topk, i); };
+
   // tile prefix sums
   int64_t sum = 0;
-  for (int i = lo; i < hi; ++i) sum += stream_tiles(seqlens, topk, i);
+  for (int i = lo; i < hi; ++i) {
+    const int64_t t = stream_tiles(seqlens, topk, i);
+    if (in_lds) lds_tiles[i] = (int32_t)t;
+    sum += t;
+  }
   int64_t N;
   int64_t acc = block_exclusive_scan(sum, wave_sums, N);
   for (int i = lo; i < hi; ++i) {
     first[i] = (int32_t)acc;
-    acc += stream_tiles(seqlens, topk, i);
+    acc += tiles_of(i);
   }
   if (tid == 0) first[n] = (int32_t)N;
   int64_t q = (N + W - 1) / W;
@@ -100,14 +107,14 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t*
   // splits per stream = workers meeting it
   sum = 0;
   for (int i = lo; i < hi; ++i) {
-    const int64_t t = stream_tiles(seqlens, topk, i);
+    const int64_t t = tiles_of(i);
     sum += t == 0 ? 0 : ((int64_t)first[i] + t - 1) / q - (int64_t)first[i] / q + 1;
   }
   int64_t total_splits;
   acc = block_exclusive_scan(sum, wave_sums, total_splits);
   for (int i = lo; i < hi; ++i) {
     split_off[i] = (int32_t)acc;
-    const int64_t t = stream_tiles(seqlens, topk, i);
+    const int64_t t = tiles_of(i);
     acc += t == 0 ? 0 : ((int64_t)first[i] + t - 1) / q - (int64_t)first[i] / q + 1;
   }
   if (tid == 0) split_off[n] = (int32_t)total_splits;
