@@ -143,6 +143,18 @@ def test_split_lengths_every_variant(is_fp8, topk, W):
     check_problem(prob, num_workers=W, what="%s topk=%d W=%d" % ("fp8" if is_fp8 else "bf16", topk, W))
 
 
+@pytest.mark.parametrize("is_fp8,topk", [(False, 0), (True, 0), (False, 320), (True, 320)],
+                         ids=["dense bf16", "dense fp8", "sparse bf16", "sparse fp8"])
+@pytest.mark.parametrize("s_q,W", [(1, 3), (3, 7)])
+def test_partial_row_tiles_every_variant(is_fp8, topk, s_q, W):
+    """40 query heads: each stream's last (or only) 64-row tile is partial, so Q
+    rows past the stream load as zeros and only the existing rows are written
+    back; few workers, so a workgroup runs several pieces (streams) in turn."""
+    prob = mi.make_problem("partial rows", 3, s_q, 40, [900, 95, 400], seed=60 + W, topk=topk, is_fp8=is_fp8,
+                           n_invalid=5 if topk else 0, recipe="clip")
+    check_problem(prob, num_workers=W, what="%s topk=%d s_q=%d W=%d" % ("fp8" if is_fp8 else "bf16", topk, s_q, W))
+
+
 # --------------------------------------------------------------------------------------
 # edge cases
 
