@@ -160,13 +160,22 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
   const int r4 = wave_s & 3, tb = wave_s >> 2;  // scalars
   const int qrow = 16 * r4 + l16;  // this lane's query row (0..63) in the score and softmax steps
 
-  // workgroup -> (worker, row tile); the row tiles of one worker share an XCD
+  // workgroup -> (worker, row tile).  Workgroups are dealt to the 8 XCDs in turn
+  // (XCD = blockIdx mod 8).  The row tiles of one worker share an XCD, so the
+  // second row tile reads its pages from L2; with several row tiles and whole
+  // groups of 16 workers, workers 2 x and 2 x + 1 (usually two splits of one
+  // stream, which read the same Q rows) share one as well (c4: -1.3 us; with a
+  // single row tile the pairing measured 3 us slower on c5 and is not used).
   int w, rt;
   {
     const int g = blockIdx.x;
     if (p.n_rt == 1) {
       w = g;
       rt = 0;
+    } else if ((p.W & 15) == 0) {
+      const int grp = g / (16 * p.n_rt), k = (g >> 3) % (2 * p.n_rt);
+      rt = k >> 1;
+      w = grp * 16 + 2 * (g & 7) + (k & 1);
     } else if ((p.W & 7) == 0) {
       const int grp = g / (8 * p.n_rt), rem = g % (8 * p.n_rt);
       rt = rem >> 3;
