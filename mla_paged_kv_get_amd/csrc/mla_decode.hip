@@ -824,9 +824,23 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       }
 
       // the restart must be taken by the whole workgroup (it contains barriers);
-      // the vote is over every lane, so it is taken before the lane-0 store
+      // the vote is over every lane, so it is taken before the lane-0 store.
+      // The same barrier publishes l and m_ref of each row for the epilogue
+      // (l of a row: this lane's sum over its tokens, over the 4 lanes of the row
+      // and the two token blocks); a restarted pass recomputes both.
       const bool wave_overflow = __ballot(overflow) != 0;
       if (lane == 0) wflag[wave_s] = wave_overflow ? 1 : 0;
+      l_sum += __shfl_xor(l_sum, 16);
+      l_sum += __shfl_xor(l_sum, 32);
+      {
+        int lo = lane;
+        asm volatile("" : "+v"(lo));  // the row index is formed here, not kept live across the loop
+        const int qr = 16 * r4 + (lo & 15);
+        if (lo < 16) {
+          xrow[tb * 64 + qr] = l_sum;
+          if (tb == 0) xrow[128 + qr] = m_ref;
+        }
+      }
       __syncthreads();
       redo = false;
 #pragma unroll
@@ -835,30 +849,18 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       ++pass;
       if (redo) {
         // the split's row maximum over every lane and token block holding the row
+        // (no wave reads the rows' l and m_ref once a restart is decided)
         const float ms = row_max16(m_seen);
         if (h4 == 0) xrow[tb * 64 + qrow] = ms;
         __syncthreads();
         const float m0 = fmaxf(xrow[qrow], xrow[64 + qrow]);
         m_ref = m0 == kNegInf ? kNegInf : m0 + kRefLift;
+        // (xrow and wflag are next written at the end of the restarted pass,
+        // after its rounds' barriers)
       }
-      __syncthreads();
     } while (redo);
 
     // ---- epilogue -------------------------------------------------------------------
-    // l of each row: this lane's sum over its tokens, over the 4 lanes of the row
-    // and the two token blocks; m_ref of each row from its score waves.
-    l_sum += __shfl_xor(l_sum, 16);
-    l_sum += __shfl_xor(l_sum, 32);
-    {
-      int lo = lane;
-      asm volatile("" : "+v"(lo));  // the row index is formed here, not kept live across the loop
-      const int qr = 16 * r4 + (lo & 15);
-      if (lo < 16) {
-        xrow[tb * 64 + qr] = l_sum;
-        if (tb == 0) xrow[128 + qr] = m_ref;
-      }
-    }
-    __syncthreads();
     // The normalised rows go through LDS (the free tile buffers, rows padded by
     // 16 bytes against bank conflicts) so that the global stores are whole
     // contiguous runs: the tile's rows are contiguous in o and in the split's
