@@ -135,6 +135,34 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
                                     int is_fp8, int causal, void* workspace, size_t workspace_bytes, void* o,
                                     float* lse, void* stream);
 
+/*
+ * Sparse prefill: token-sparse attention of many query tokens over one
+ * contiguous latent KV sequence ("FlashMLA" summary on agentlenshq.com, usage
+ * section, the sparse prefill call flash_mla_sparse_fwd(q, kv, indices, ...):
+ * a query tensor, the KV and a 3-D index tensor naming the KV tokens each query
+ * token attends; zhouruolin.cn FlashMLA page, test section, sparse prefill).
+ * The pages leave the rest open; this call reads it plainly: BF16 KV, one KV
+ * head, and per query row s the same rule as sparse decoding,
+ *   o = softmax(softmax_scale * q K_T^T) V_T,  lse = ln sum exp(softmax_scale * q K_T^T),
+ * with T the non-(-1) entries of indices[s, 0:topk] (duplicates count with
+ * multiplicity; an empty T gives o = 0, lse = -inf).
+ *   q          device bf16 [s_q, h_q, 576]
+ *   kv         device bf16 [s_kv, 576] (token j = row j; h_kv = 1)
+ *   indices    device int32 [s_q, topk], entries in {-1} U [0, s_kv) (not
+ *              checked on the device)
+ *   o, lse     device bf16 [s_q, h_q, 512] and fp32 [s_q, h_q] (outputs)
+ *   workspace  device buffer of the size call's workspace_bytes: the call
+ *              writes the sequence's page table and the schedule there, then
+ *              runs the sparse decode path on it (four launches on `stream`)
+ * num_workers and softmax_scale as for mla_decode_with_kvcache.  Errors as for
+ * the other calls; nothing is launched when one is returned.
+ */
+MLA_API int mla_sparse_prefill_workspace_size(int s_q, int h_q, int h_kv, int64_t s_kv, int topk, int num_workers,
+                                              size_t* workspace_bytes, int* num_workers_out);
+MLA_API int mla_sparse_prefill(const void* q, const void* kv, int64_t s_kv, const int32_t* indices, int s_q, int h_q,
+                               int h_kv, int topk, int d_qk, int d_v, float softmax_scale, int num_workers,
+                               void* workspace, size_t workspace_bytes, void* o, float* lse, void* stream);
+
 /* Thread-local, NUL-terminated description of this thread's last failed call ("" if none). */
 MLA_API const char* mla_last_error(void);
 

@@ -210,6 +210,23 @@ def make_problem(name: str, B: int, s_q: int, h_q: int, seqlens: Sequence[int], 
     return prob
 
 
+def make_prefill_problem(name: str, s_q: int, h_q: int, s_kv: int, topk: int, *, seed: int, n_invalid: int = 0,
+                         recipe: str = "sample") -> Problem:
+    """A sparse prefill call as a one-request problem: one contiguous KV sequence
+    of s_kv tokens (N(0,1) latents in bf16), whose pages are its consecutive
+    64-token pieces (identity block table), and s_q query tokens with their own
+    topk index lists.  The prefill call reads kvcache.view(-1, 576)[:s_kv], q[0]
+    and indices[0]."""
+    gen = torch.Generator().manual_seed(seed)
+    n_pages = (int(s_kv) + PAGE - 1) // PAGE
+    q = torch.randn((1, s_q, h_q, D_QK), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    kv = _fill_cache(gen, n_pages, False)
+    indices = _sparse_indices(gen, [int(s_kv)], s_q, topk, n_invalid, recipe)
+    return Problem(name=name, q=q, kvcache=kv, block_table=torch.arange(n_pages, dtype=torch.int32).view(1, -1),
+                   cache_seqlens=torch.tensor([int(s_kv)], dtype=torch.int32), indices=indices, is_fp8=False,
+                   softmax_scale=1.0 / math.sqrt(D_QK), meta=dict(seed=seed, recipe=recipe, n_invalid=n_invalid))
+
+
 def attended_mask(prob: Problem) -> torch.Tensor:
     """bool [num_blocks, 64]: which stored tokens any query row can reach."""
     mask = torch.zeros((prob.num_blocks, PAGE), dtype=torch.bool)

@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_with_kvcache.restype = I
         L.mla_decode_with_kvcache.argtypes = [P, P, I64, P, I, P, I, I, I, I, I, I, ctypes.c_float, P, Z, I, P, I, I, I,
                                               P, Z, P, P, P]
+        L.mla_sparse_prefill_workspace_size.restype = I
+        L.mla_sparse_prefill_workspace_size.argtypes = [I, I, I, I64, I, I, ctypes.POINTER(Z), ctypes.POINTER(I)]
+        L.mla_sparse_prefill.restype = I
+        L.mla_sparse_prefill.argtypes = [P, P, I64, P, I, I, I, I, I, I, ctypes.c_float, I, P, Z, P, P, P]
         L.mla_debug_dequant_fp8.restype = I
         L.mla_debug_dequant_fp8.argtypes = [P, I64, P, P]
         L.mla_set_decode_kernel_events.restype = I
@@ -185,6 +189,47 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
             s_q, h_q, m.h_kv, D_QK, d_v, scale, _ptr(m.tensor), m.tensor.numel() * 4, m.num_workers, _ptr(indices),
             topk, int(is_fp8), int(bool(causal)), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _ptr(out), _ptr(lse), _stream(dev)), "mla_decode_with_kvcache")
+    return out, lse
+
+
+def mla_sparse_prefill(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
+                       softmax_scale: Optional[float] = None, num_workers: int = 0,
+                       workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """o (bf16 [s_q, h_q, 512]) and lse (fp32 [s_q, h_q]) of token-sparse prefill.
+
+    q: bf16 [s_q, h_q, 576]; kv: bf16 [s_kv, (1,) 576], one contiguous sequence;
+    indices: int32 [s_q, (1,) topk] of positions in [0, s_kv) or -1 (skipped).
+    """
+    dev = q.device
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != D_QK:
+        raise ValueError("q must be bf16 [s_q, h_q, 576]")
+    s_q, h_q = int(q.shape[0]), int(q.shape[1])
+    if kv.dtype != torch.bfloat16 or kv.shape[-1] != D_QK or kv.numel() % D_QK:
+        raise ValueError("kv must be bf16 [s_kv, (1,) 576]")
+    s_kv = kv.numel() // D_QK
+    if indices.dtype != torch.int32 or indices.shape[0] != s_q or indices.dim() not in (2, 3):
+        raise ValueError("indices must be int32 [s_q, (1,) topk]")
+    topk = int(indices.shape[-1])
+    for name, t in (("q", q), ("kv", kv), ("indices", indices)):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("%s must be contiguous and on %s" % (name, dev))
+    need, W = ctypes.c_size_t(0), ctypes.c_int(0)
+    with torch.cuda.device(dev):
+        _check(lib().mla_sparse_prefill_workspace_size(s_q, h_q, 1, s_kv, topk, int(num_workers), ctypes.byref(need),
+                                                       ctypes.byref(W)), "mla_sparse_prefill_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((s_q, h_q), dtype=torch.float32, device=dev)
+    scale = float(softmax_scale) if softmax_scale is not None else 1.0 / math.sqrt(D_QK)
+    with torch.cuda.device(dev):
+        _check(lib().mla_sparse_prefill(
+            _ptr(q), _ptr(kv), s_kv, _ptr(indices), s_q, h_q, 1, topk, D_QK, D_V, scale, int(num_workers),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev)),
+            "mla_sparse_prefill")
     return out, lse
 
 

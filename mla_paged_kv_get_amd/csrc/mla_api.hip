@@ -99,6 +99,32 @@ void sizes(const Shape& s, int W, size_t* meta, size_t* part_o, size_t* ws) {
   *ws = *part_o + align_up(max_splits * (size_t)s.R * sizeof(float));
 }
 
+// Sparse prefill workspace: the single request's length (int32), its identity
+// page table (one int32 per 64-token piece of the sequence), the scheduler's
+// metadata and the decode workspace, each 256-byte aligned.
+struct PrefillLayout {
+  size_t pages_off, meta_off, meta_bytes, ws_off, ws_bytes, total;
+  int n_pages, W;
+};
+
+int prefill_layout(int s_q, int h_q, int h_kv, int64_t s_kv, int topk, int num_workers, PrefillLayout* L) {
+  if (s_kv < 1 || s_kv > INT32_MAX - mla::kPage) return fail(MLA_ERR_INVALID_ARG, "s_kv must be in [1, 2^31 - 65]");
+  if (topk < 1) return fail(MLA_ERR_INVALID_ARG, "sparse prefill needs topk >= 1 (got %d)", topk);
+  Shape s;
+  int rc = shape_of(1, s_q, h_q, h_kv, topk, &s);
+  if (rc != MLA_OK) return rc;
+  rc = resolve_workers(num_workers, s, &L->W);
+  if (rc != MLA_OK) return rc;
+  size_t part_o;
+  sizes(s, L->W, &L->meta_bytes, &part_o, &L->ws_bytes);
+  L->n_pages = (int)((s_kv + mla::kPage - 1) / mla::kPage);
+  L->pages_off = kAlign;
+  L->meta_off = align_up(L->pages_off + (size_t)L->n_pages * sizeof(int32_t));
+  L->ws_off = align_up(L->meta_off + L->meta_bytes);
+  L->total = L->ws_off + L->ws_bytes;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,6 +255,45 @@ MLA_API int mla_debug_dequant_fp8(const uint8_t* tokens, int64_t n, void* out, v
   const hipError_t e = mla::launch_debug_dequant(tokens, n, (uint16_t*)out, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "dequant launch");
   return MLA_OK;
+}
+
+MLA_API int mla_sparse_prefill_workspace_size(int s_q, int h_q, int h_kv, int64_t s_kv, int topk, int num_workers,
+                                              size_t* workspace_bytes, int* num_workers_out) {
+  g_err[0] = 0;
+  if (!workspace_bytes) return fail(MLA_ERR_INVALID_ARG, "null size output pointer");
+  PrefillLayout L;
+  const int rc = prefill_layout(s_q, h_q, h_kv, s_kv, topk, num_workers, &L);
+  if (rc != MLA_OK) return rc;
+  *workspace_bytes = L.total;
+  if (num_workers_out) *num_workers_out = L.W;
+  return MLA_OK;
+}
+
+MLA_API int mla_sparse_prefill(const void* q, const void* kv, int64_t s_kv, const int32_t* indices, int s_q, int h_q,
+                               int h_kv, int topk, int d_qk, int d_v, float softmax_scale, int num_workers,
+                               void* workspace, size_t workspace_bytes, void* o, float* lse, void* stream) {
+  g_err[0] = 0;
+  if (!q || !kv || !indices || !workspace || !o || !lse) return fail(MLA_ERR_INVALID_ARG, "null pointer argument");
+  if (d_qk != mla::kDQK || d_v != mla::kDV)
+    return fail(MLA_ERR_UNSUPPORTED, "only d_qk = 576 and d_v = 512 are supported (got %d, %d)", d_qk, d_v);
+  if ((((uintptr_t)q) | ((uintptr_t)kv) | ((uintptr_t)o) | ((uintptr_t)workspace)) & 15)
+    return fail(MLA_ERR_INVALID_ARG, "q, kv, o and workspace must be 16-byte aligned");
+  PrefillLayout L;
+  int rc = prefill_layout(s_q, h_q, h_kv, s_kv, topk, num_workers, &L);
+  if (rc != MLA_OK) return rc;
+  if (workspace_bytes < L.total)
+    return fail(MLA_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
+  char* ws = (char*)workspace;
+  int32_t* seqlen = (int32_t*)ws;
+  int32_t* pages = (int32_t*)(ws + L.pages_off);
+  int32_t* meta = (int32_t*)(ws + L.meta_off);
+  hipError_t e = mla::launch_prefill_setup(seqlen, pages, L.n_pages, (int)s_kv, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill set-up launch");
+  e = mla::launch_sched(seqlen, 1, s_q, h_q, topk, L.W, min_tiles_for(0, topk), meta, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "scheduler launch");
+  return mla_decode_with_kvcache(q, kv, L.n_pages, pages, L.n_pages, seqlen, 1, s_q, h_q, h_kv, d_qk, d_v,
+                                 softmax_scale, meta, L.meta_bytes, L.W, indices, topk, 0, 0, ws + L.ws_off,
+                                 L.ws_bytes, o, lse, stream);
 }
 
 }  // extern "C"

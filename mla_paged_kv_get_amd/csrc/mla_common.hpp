@@ -84,6 +84,7 @@ hipError_t launch_sched(const int32_t* seqlens, int B, int s_q, int h_q, int top
                         int32_t* meta, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool is_fp8, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_prefill_setup(int32_t* seqlen, int32_t* pages, int n_pages, int s_kv, hipStream_t stream);
 hipError_t launch_debug_dequant(const uint8_t* tokens, int64_t n, uint16_t* out, hipStream_t stream);
 
 }  // namespace mla

@@ -31,7 +31,8 @@ def L():
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     assert set(syms) == {"mla_get_metadata_size", "mla_get_metadata", "mla_decode_with_kvcache", "mla_last_error",
-                         "mla_debug_dequant_fp8", "mla_set_decode_kernel_events"}
+                         "mla_debug_dequant_fp8", "mla_set_decode_kernel_events",
+                         "mla_sparse_prefill_workspace_size", "mla_sparse_prefill"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -124,3 +125,30 @@ def test_decode_kernel_events_hook_needs_both_or_neither(L):
     assert "both" in L.mla_last_error().decode()
     assert f(None, ctypes.c_void_p(0x1000)) == -1
     assert f(None, None) == 0  # clearing is always fine (no HIP call is made)
+
+
+def prefill_size(L, s_q, h_q, s_kv, topk, W=64, h_kv=1):
+    L.mla_sparse_prefill_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                                    ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t),
+                                                    ctypes.POINTER(ctypes.c_int)]
+    wb, w = ctypes.c_size_t(0), ctypes.c_int(0)
+    rc = L.mla_sparse_prefill_workspace_size(s_q, h_q, h_kv, s_kv, topk, W, ctypes.byref(wb), ctypes.byref(w))
+    return rc, wb.value, w.value
+
+
+def test_sparse_prefill_workspace_size(L):
+    """The prefill workspace holds the sequence length, one page-table entry per
+    64 tokens, the schedule of s_q streams and the sparse decode workspace, in
+    256-byte aligned parts; bad shapes are refused before anything runs."""
+    rc, wb, w = prefill_size(L, 4096, 128, 8192, 2048, W=128)
+    assert rc == 0 and w == 128
+    rc_m, mb, dwb, _ = sizes(L, 1, 4096, 128, topk=2048, W=128)
+    assert rc_m == 0
+    pages = -(-8192 // 64) * 4
+    assert wb == 256 + -(-pages // 256) * 256 + -(-mb // 256) * 256 + dwb
+    assert prefill_size(L, 16, 64, 8193, 64)[1] > prefill_size(L, 16, 64, 8192, 64)[1] - 1
+    for bad in (dict(topk=0), dict(s_kv=0), dict(h_kv=2), dict(s_q=0), dict(h_q=0)):
+        kw = dict(s_q=16, h_q=64, s_kv=1000, topk=64)
+        kw.update(bad)
+        rc, _, _ = prefill_size(L, **kw)
+        assert rc < 0, bad

@@ -310,3 +310,34 @@ def test_causal_rejected_for_sparse():
     prob = mi.make_problem("causal sparse", 1, 2, 16, [300], seed=96, topk=64)
     with pytest.raises(mla.MlaError, match="causal"):
         run_gpu(prob, 0, causal=True)
+
+
+# --------------------------------------------------------------------------------------
+# sparse prefill: many query tokens over one contiguous KV sequence, through the
+# same sparse path (the oracle sees it as one request with an identity page table)
+
+PREFILL = [
+    dict(name="prefill s_q=48 h64", s_q=48, h_q=64, s_kv=700, topk=128, n_invalid=5, seed=101),
+    dict(name="prefill h128 topk past s_kv (clip)", s_q=20, h_q=128, s_kv=100, topk=256, recipe="clip", seed=102),
+    dict(name="prefill h40 partial rows", s_q=33, h_q=40, s_kv=3000, topk=512, n_invalid=9, seed=103),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[c["name"] for c in PREFILL])
+@pytest.mark.parametrize("W", [0, 7])
+def test_sparse_prefill(case, W):
+    import mla_paged_kv_get_amd as mla
+
+    c = dict(case)
+    prob = mi.make_prefill_problem(c.pop("name"), **c)
+    say("[gpu] %s (W=%s)" % (prob.name, W or "auto"))
+    dev = torch.device("cuda:0")
+    s_kv = int(prob.cache_seqlens[0])
+    q = prob.q[0].to(dev)
+    kv = prob.kvcache.reshape(-1, 576)[:s_kv].contiguous().to(dev)
+    idx = prob.indices[0].to(dev)
+    o, lse = mla.mla_sparse_prefill(q, kv, idx, softmax_scale=prob.softmax_scale, num_workers=W)
+    torch.cuda.synchronize()
+    o, lse = flat(o, lse)
+    o_ref, lse_ref = oracle.problem_decode(prob)
+    compare(o, lse, o_ref, lse_ref, prob.name)
