@@ -34,6 +34,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -60,6 +61,8 @@ def parse():
     ap.add_argument("--workloads", default="2", help="comma list of configurations; 2 (the headline) is always run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--prefill", action="store_true",
+                    help="also time the sparse prefill call (s_q 2048 query tokens, h_q 128, s_kv 8192, topk 2048)")
     ap.add_argument("--no-headline", action="store_true",
                     help="run only the --workloads listed (the first one is reported); for per-workload profiles")
     ap.add_argument("--no-calls", action="store_true",
@@ -241,6 +244,49 @@ def cpu_baseline(prob):
                 seconds=round(dt, 2), gbps=round(prob.bytes() / dt / 1e9, 3))
 
 
+PREFILL_SHAPE = dict(s_q=2048, h_q=128, s_kv=8192, topk=2048, n_invalid=102)
+
+
+def measure_prefill(steps: int, warmup: int):
+    """Whole sparse prefill calls (set-up, schedule, decode path, combine) back to
+    back, timed by one event pair; FLOPs = 2 (576 + 512) per row per attended token."""
+    import torch
+
+    import mla_inputs as mi
+    import mla_paged_kv_get_amd as mla
+
+    sh = PREFILL_SHAPE
+    prob = mi.make_prefill_problem("sparse prefill (s_q %d, h_q %d, s_kv %d, topk %d)" % (
+        sh["s_q"], sh["h_q"], sh["s_kv"], sh["topk"]), sh["s_q"], sh["h_q"], sh["s_kv"], sh["topk"], seed=7,
+        n_invalid=sh["n_invalid"])
+    dev = torch.device("cuda:0")
+    q = prob.q[0].to(dev)
+    kv = prob.kvcache.reshape(-1, 576)[:sh["s_kv"]].contiguous().to(dev)
+    idx = prob.indices[0].to(dev)
+    o = torch.empty((sh["s_q"], sh["h_q"], 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((sh["s_q"], sh["h_q"]), dtype=torch.float32, device=dev)
+    need = ctypes.c_size_t(0)
+    mla.lib().mla_sparse_prefill_workspace_size(sh["s_q"], sh["h_q"], 1, sh["s_kv"], sh["topk"], 0,
+                                                ctypes.byref(need), None)
+    ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    call = lambda: mla.mla_sparse_prefill(q, kv, idx, workspace=ws, out=o, lse=lse)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int((3000.0 * steps + 2000.0) * 2500))
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = prob.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    return dict(name=prob.name, call_us=round(ms * 1e3, 1), flops=flops, tflops=round(tflops, 1),
+                frac_mfma=round(tflops / PEAK_BF16_TFLOPS, 4))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -287,6 +333,11 @@ def main():
                 hbm_gbps_step=round(head_prob.bytes() / (h["step_us"] * 1e-6) / 1e9, 1),
                 roofline=roofline,
                 workloads={str(c): r for c, r in results.items()})
+    if args.prefill:
+        pf = measure_prefill(max(3, min(args.steps, 20)), 2)
+        print("[bench] %s: call %.1f us (%.1f TFLOP/s, %.1f %% of MFMA peak)" % (
+            pf["name"], pf["call_us"], pf["tflops"], 100 * pf["frac_mfma"]), file=sys.stderr, flush=True)
+        line["workloads"]["prefill"] = pf
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head_prob)
     print(json.dumps(line))
