@@ -226,6 +226,8 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
   p.W = W;
   p.causal = causal;
   p.scale_log2 = scale * 1.4426950408889634f;
+  const uint64_t pool_bytes = (uint64_t)num_blocks * mla::kPage * (is_fp8 ? mla::kFp8TokenBytes : mla::kBf16TokenBytes);
+  p.pool_records = pool_bytes <= 0xFFFFFF00ull ? (uint32_t)pool_bytes : 0u;
   hipError_t e = hipSuccess;
   if (g_ev_start && (e = hipEventRecord(g_ev_start, (hipStream_t)stream)) != hipSuccess)
     return hip_fail(e, "decode start event");

@@ -77,6 +77,7 @@ struct DecodeParams {
   int W;                     // workers
   int causal;                // dense: query token s of s_q sees positions <= seqlen - s_q + s
   float scale_log2;          // softmax_scale * log2(e)
+  uint32_t pool_records;     // sparse BF16: KV pool bytes when at most 0xFFFFFF00 (MUBUF gathers), else 0
 };
 
 // Launchers (each in its own .hip file).

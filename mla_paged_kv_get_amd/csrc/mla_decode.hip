@@ -123,6 +123,9 @@ constexpr int kLoads = 5;
 constexpr int kOutRowBf16 = kDV * 2 + 16;
 constexpr int kOutRowF32 = kDV * 4 + 16;
 static_assert(kRowTile * kOutRowF32 <= kNBuf * kSubBytes, "output staging fits the tile buffers");
+// a gather offset past every pool the MUBUF gathers are used for (their
+// resource covers at most kPastPool bytes, and kPastPool + 16 does not wrap)
+constexpr uint32_t kPastPool = 0xFFFFFF00u;
 constexpr int kFp8Loads = 9;  // vector memory operations of one FP8 sub-tile load (4 codes, 4 scales, RoPE)
 static_assert(kSlots == 4 * kDecThreads + kDecThreads / 2, "staging split");
 // Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle.
@@ -140,7 +143,10 @@ struct RawFp8 {
   u32x2 r;
 };
 
-template <bool FP8, bool SPARSE>
+// BUFG (sparse BF16): token gathers as MUBUF loads against one resource over
+// the whole KV pool (pools below 4 GiB), where a skipped slot's offset lies
+// past the pool and loads zeros; else FLAT loads from per-lane addresses.
+template <bool FP8, bool SPARSE, bool BUFG>
 __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
@@ -433,12 +439,19 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     // zero token when a slot is not attended).  stage_begin reads the
     // sub-tile's ring entry; stage_load issues piece k.
     __amdgpu_buffer_rsrc_t st_rs;  // dense: the sub-tile's bytes inside the sequence
-    int st_tok = -1;               // sparse: token row of slot l32
+    int st_tk[kLoads];             // sparse: token row (or -1) of each of this thread's pieces
     auto stage_begin = [&](int u) {
       if constexpr (SPARSE) {
         const int idx = idx_slot(u)[l32];
         const int pg = pg_slot(u)[l32];
-        st_tok = (slot_ok(u) && idx >= 0) ? pg * kPage + (idx & 63) : -1;
+        const int tok = (slot_ok(u) && idx >= 0) ? pg * kPage + (idx & 63) : -1;
+        // each piece's token row, fetched from its slot's lane here, so that the
+        // loads between the score MFMAs need no cross-lane (LDS) operation whose
+        // wait would also wait for the K fragments in flight
+        int to = tid;
+        asm volatile("" : "+v"(to));
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) st_tk[k] = __shfl(tok, min(k * kDecThreads + to, kSlots - 1) / kTokenChunks);
       } else {
         const int page = __builtin_amdgcn_readfirstlane(pg_slot(u)[0]);
         const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
@@ -456,10 +469,18 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         asm volatile("" : "+v"(to));
         const int s = min(k * kDecThreads + to, kSlots - 1);
         const int tt = s / kTokenChunks;
-        const int tk = __shfl(st_tok, tt);
-        const uint8_t* src = (tk >= 0 ? p.kv + (int64_t)tk * kBf16TokenBytes : g_zero_token) +
-                             ((s - tt * kTokenChunks) ^ tile_swizzle(tt)) * 16;
-        global_load_lds16((const void*)src, dst);
+        const int tk = st_tk[k];
+        const uint32_t chunk = (uint32_t)((s - tt * kTokenChunks) ^ tile_swizzle(tt)) * 16u;
+        if constexpr (BUFG) {
+          // MUBUF keeps the compiler's wait counts exact (a FLAT load into LDS
+          // makes every later wait a full drain)
+          const __amdgpu_buffer_rsrc_t pool_rs =
+              __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, 0, p.pool_records, kBufferFlags);
+          buffer_load_lds16(pool_rs, dst, tk >= 0 ? (uint32_t)tk * (uint32_t)kBf16TokenBytes + chunk : kPastPool);
+        } else {
+          const uint8_t* src = (tk >= 0 ? p.kv + (int64_t)tk * kBf16TokenBytes : g_zero_token) + chunk;
+          global_load_lds16((const void*)src, dst);
+        }
       } else {
         const int t = slot_token(k);
         buffer_load_lds16(st_rs, dst, (uint32_t)(t * kBf16TokenBytes + slot_src(k, t)));
@@ -941,10 +962,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
   }
 }
 
-template <bool FP8, bool SPARSE>
+template <bool FP8, bool SPARSE, bool BUFG>
 hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
   static bool attr_set = false;
-  auto kern = mla_decode_kernel<FP8, SPARSE>;
+  auto kern = mla_decode_kernel<FP8, SPARSE, BUFG>;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
@@ -958,8 +979,9 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams& p, bool is_fp8, hipStream_t stream) {
   const bool sparse = p.topk > 0;
-  if (is_fp8) return sparse ? launch_variant<true, true>(p, stream) : launch_variant<true, false>(p, stream);
-  return sparse ? launch_variant<false, true>(p, stream) : launch_variant<false, false>(p, stream);
+  if (is_fp8) return sparse ? launch_variant<true, true, false>(p, stream) : launch_variant<true, false, false>(p, stream);
+  if (!sparse) return launch_variant<false, false, false>(p, stream);
+  return p.pool_records != 0 ? launch_variant<false, true, true>(p, stream) : launch_variant<false, true, false>(p, stream);
 }
 
 }  // namespace mla

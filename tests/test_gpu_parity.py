@@ -341,3 +341,25 @@ def test_sparse_prefill(case, W):
     o, lse = flat(o, lse)
     o_ref, lse_ref = oracle.problem_decode(prob)
     compare(o, lse, o_ref, lse_ref, prob.name)
+
+
+def test_sparse_bf16_pool_past_4gib():
+    """Sparse BF16 gathers from pools under 4 GiB go through one buffer resource
+    over the pool; larger pools take per-lane addresses.  The same problem's pages
+    placed at the top of a 4.3 GB pool (so every gathered token lies past 4 GiB)
+    must give the oracle's result too."""
+    prob = mi.make_problem("sparse bf16 in a 4.3 GB pool", 2, 1, 64, [900, 300], seed=111, topk=192, n_invalid=11)
+    d = to_device(prob)
+    n = prob.num_blocks
+    big_pages = (int(4.3e9) // (64 * 576 * 2)) + n
+    big = torch.empty((big_pages, 64, 576), dtype=torch.bfloat16, device=DEV)
+    big[big_pages - n:] = d["kvcache"]
+    d["kvcache"] = big
+    d["block_table"] = d["block_table"] + (big_pages - n)
+    say("[gpu] %s (%d pages, %.2f GB)" % (prob.name, big_pages, big.numel() * 2 / 1e9))
+    o, lse, _ = run_gpu(prob, num_workers=5, dev_inputs=d)
+    del big, d
+    torch.cuda.empty_cache()
+    o, lse = flat(o, lse)
+    o_ref, lse_ref = oracle.problem_decode(prob)
+    compare(o, lse, o_ref, lse_ref, prob.name)
