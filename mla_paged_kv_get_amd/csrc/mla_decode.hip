@@ -496,23 +496,33 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     // entries go to scalars and their addresses are scalar arithmetic; a token
     // that is not attended (or lies past the sequence or the split) reads the
     // zero token.
-    auto load_fp8 = [&](int u, RawFp8& r) {
+    // The ring entries a tile load of sub-tile u needs (sparse: its four token
+    // rows; dense: its page).  Waiting for an LDS read also waits for every
+    // older one, so a dense round reads its page before its K fragments.
+    struct Fp8Rows {
+      int v[4];
+    };
+    auto fp8_rows = [&](int u) -> Fp8Rows {
+      Fp8Rows t;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t.v[k] = SPARSE ? pg_slot(u)[8 * k + wave_s] : (k == 0 ? pg_slot(u)[0] : 0);
+      return t;
+    };
+    auto load_fp8 = [&](int u, RawFp8& r, const Fp8Rows& rows) {
       int lo = lane;
       asm volatile("" : "+v"(lo));  // per-lane offsets recomputed here, not kept live
       const uint8_t* pt[4];
       if constexpr (SPARSE) {
         int tk[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) tk[k] = pg_slot(u)[8 * k + wave_s];
-#pragma unroll
         for (int k = 0; k < 4; ++k) {
-          tk[k] = __builtin_amdgcn_readfirstlane(tk[k]);
+          tk[k] = __builtin_amdgcn_readfirstlane(rows.v[k]);
           pt[k] = u < u1 && tk[k] >= 0 ? p.kv + (int64_t)tk[k] * tok_bytes : g_zero_token;
         }
       } else {
         // past the split the ring slot may never have been written: its page is not used
         const int valid = u < u1 ? seqlen - u * kSub : 0;  // tokens of the sub-tile in the sequence
-        const int page = __builtin_amdgcn_readfirstlane(pg_slot(u)[0]);
+        const int page = __builtin_amdgcn_readfirstlane(rows.v[0]);
         const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * tok_bytes;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -608,14 +618,14 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
           }
           lds_barrier();
         }
-        load_fp8(u0, raw[0]);
-        load_fp8(u0 + 1, raw[1]);
+        load_fp8(u0, raw[0], fp8_rows(u0));
+        load_fp8(u0 + 1, raw[1], fp8_rows(u0 + 1));
         stage_q(0, buffer(u0 + 2));
         stage_q(1, buffer(u0 + 3));
         store_fp8(raw[0], buffer(u0));
         store_fp8(raw[1], buffer(u0 + 1));
-        load_fp8(u0 + 2, raw[0]);
-        load_fp8(u0 + 3, raw[1]);
+        load_fp8(u0 + 2, raw[0], fp8_rows(u0 + 2));
+        load_fp8(u0 + 3, raw[1], fp8_rows(u0 + 3));
         // Q's direct loads are older than the 2 x 9 register loads just issued
         barrier_keep_seen<2 * kFp8Loads>();
         read_q(buffer(u0 + 2), buffer(u0 + 3));
@@ -709,6 +719,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         constexpr int kSet = decltype(set_tag)::value;  // FP8: the VGPR set this round stores and refills
         const bool issue = kIssue == 1 || u + 3 < u1;  // sub-tile u + 3 exists (workgroup-uniform)
         __builtin_amdgcn_sched_barrier(0);
+        // FP8 dense: the page of sub-tile u + 4, read before this round's K
+        // fragments (sparse: its four token rows are read at the load; holding
+        // them across the first score MFMAs costs the registers it lacks)
+        Fp8Rows nrows;
+        if constexpr (FP8 && !SPARSE) nrows = fp8_rows(u + 4);
         // staging work placed after score MFMA kk
         auto stage_step = [&](int kk) __attribute__((always_inline)) {
           if constexpr (FP8) {
@@ -720,7 +735,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
               if (!kFirst) fp8_meta_publish(u - 1, fmeta[kSet ^ 1]);
             }
             if (kk == 2) fmeta[kSet] = fp8_meta_load(u);
-            if (kk == 3) load_fp8(u + 4, raw[kSet]);
+            if (kk == 3) {
+              if constexpr (SPARSE)
+                load_fp8(u + 4, raw[kSet], fp8_rows(u + 4));
+              else
+                load_fp8(u + 4, raw[kSet], nrows);
+            }
           } else {
             if (issue) {
               if (kk == 0) stage_begin(u + 3);
