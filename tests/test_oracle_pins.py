@@ -472,3 +472,28 @@ def test_causal_rejects_sparse():
     prob = mi.make_problem("cs", 1, 2, 2, [100], seed=86, topk=16)
     with pytest.raises(ValueError):
         run_oracle(prob, causal=True)
+
+
+def test_sparse_prefill_problem_is_plain_gather_attention():
+    """A sparse prefill problem (one contiguous KV sequence, identity page table)
+    reaches the oracle as a one-request sparse decode; its result must equal
+    attention written directly on the contiguous rows: for query token s, the
+    rows kv[indices[s]] (-1 dropped) as K, their first 512 dims as V, in float64."""
+    prob = mi.make_prefill_problem("prefill pin", 6, 3, 150, 40, seed=17, n_invalid=7, recipe="clip")
+    o, lse = run_oracle(prob)
+    o = o.reshape(6, 3, 512)
+    lse = lse.reshape(6, 3)
+    kv = prob.kvcache.reshape(-1, 576)[:150].double()
+    q = prob.q[0].double()
+    for s in range(6):
+        rows = prob.indices[0, s].long()
+        rows = rows[rows >= 0]
+        k = kv[rows]
+        for h in range(3):
+            logits = prob.softmax_scale * (k @ q[s, h])
+            m = logits.max()
+            w = torch.exp(logits - m)
+            ref_o = (w[:, None] * k[:, :512]).sum(0) / w.sum()
+            ref_lse = float(m + torch.log(w.sum()))
+            assert np.allclose(o[s, h], ref_o.numpy(), rtol=1e-11, atol=1e-12)
+            assert abs(lse[s, h] - ref_lse) < 1e-11
