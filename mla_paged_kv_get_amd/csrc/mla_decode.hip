@@ -270,7 +270,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     // the way it reads K.  Rows past the stream's last load as zeros: the
     // resource covers only existing rows.
     bf16x8 qf[18];
-    auto stage_q = [&](int h, MLA_LDS char* buf) {  // rows 32 h .. 32 h + 31 of the tile
+    auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((unsigned)(u - u0) & (kNBuf - 1)) * kSubBytes; };
+    // Waves 0..3 alone load Q (9 pieces per thread and half), so that waves 4..7
+    // can fetch the ring metadata meanwhile and wait for it without waiting
+    // for Q (a wave's wait for a load is a wait for all its older loads).
+    auto stage_q = [&](int h, MLA_LDS char* buf) {  // rows 32 h .. 32 h + 31 of the tile; waves 0..3
       const int r0 = rt * kRowTile + 32 * h;
       const int nrows = __builtin_amdgcn_readfirstlane(min(max(p.R_stream - r0, 0), 32));
       const __amdgpu_buffer_rsrc_t q_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -278,13 +282,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       int to = tid;
       asm volatile("" : "+v"(to));  // slot offsets computed here, not kept live across the loop
 #pragma unroll
-      for (int k = 0; k < kLoads; ++k)
-        if (k < kLoads - 1 || wave_s < 4) {
-          const int sl = min(k * kDecThreads + to, kSlots - 1);
-          const int t = sl / kTokenChunks;
-          buffer_load_lds16(q_rs, (MLA_LDS void*)(buf + k * (kDecThreads * 16) + wave_s * 1024),
-                            (uint32_t)(t * kBf16TokenBytes + ((sl - t * kTokenChunks) ^ tile_swizzle(t)) * 16));
-        }
+      for (int k = 0; k < kSlots / (kDecThreads / 2); ++k) {
+        const int sl = k * (kDecThreads / 2) + to;
+        const int t = sl / kTokenChunks;
+        buffer_load_lds16(q_rs, (MLA_LDS void*)(buf + k * (kDecThreads / 2 * 16) + wave_s * 1024),
+                          (uint32_t)(t * kBf16TokenBytes + ((sl - t * kTokenChunks) ^ tile_swizzle(t)) * 16));
+      }
     };
     auto read_q = [&](MLA_LDS char* b0, MLA_LDS char* b1) {  // rows 0..31 in b0, 32..63 in b1
       int lo = lane;
@@ -388,15 +391,29 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     // prologue: the ring entries of sub-tiles u0 .. u0 + 5 (pages) and, sparse,
     // u0 .. u0 + 7 (indices), one sub-tile per wave; ends with a barrier after
     // which they are visible
+    // (Q's loads start here too: waves 0..3 issue them and only pass the
+    // barriers, while waves 4..7 fetch the entries, two sub-tiles each, and
+    // wait for them.)
     auto meta_fill = [&]() {
-      if constexpr (SPARSE) {
-        fetch_idx(u0 + wave_s);
-        tile_barrier_drain();
-        if (wave_s < 6) fetch_pg(u0 + wave_s);
+      if (wave_s < 4) {
+        stage_q(0, buffer(u0 + 2));
+        stage_q(1, buffer(u0 + 3));
+        if constexpr (SPARSE) lds_barrier();
+        lds_barrier();
       } else {
-        if (wave_s < 6) fetch_page(u0 + wave_s);
+        const int x = wave_s - 4;
+        if constexpr (SPARSE) {
+          fetch_idx(u0 + x);
+          fetch_idx(u0 + x + 4);
+          tile_barrier_drain();
+          fetch_pg(u0 + x);
+          if (x < 2) fetch_pg(u0 + x + 4);
+        } else {
+          fetch_page(u0 + x);
+          if (x < 2) fetch_page(u0 + x + 4);
+        }
+        tile_barrier_drain();
       }
-      tile_barrier_drain();
     };
     // attended mask of sub-tile u's 32 slots (sparse)
     auto sparse_mask = [&](int u) -> uint32_t {
@@ -431,7 +448,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       }
     };
     // ---- staging ------------------------------------------------------------------
-    auto buffer = [&](int u) -> MLA_LDS char* { return smem + ((unsigned)(u - u0) & (kNBuf - 1)) * kSubBytes; };
     // BF16 direct loads of sub-tile u: this thread's five (or four) 16-byte
     // pieces.  Dense tiles use buffer loads against a resource that covers only
     // the sub-tile's tokens inside the sequence, so the pieces of tokens past
@@ -620,13 +636,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         }
         load_fp8(u0, raw[0], fp8_rows(u0));
         load_fp8(u0 + 1, raw[1], fp8_rows(u0 + 1));
-        stage_q(0, buffer(u0 + 2));
-        stage_q(1, buffer(u0 + 3));
         store_fp8(raw[0], buffer(u0));
         store_fp8(raw[1], buffer(u0 + 1));
         load_fp8(u0 + 2, raw[0], fp8_rows(u0 + 2));
         load_fp8(u0 + 3, raw[1], fp8_rows(u0 + 3));
-        // Q's direct loads are older than the 2 x 9 register loads just issued
+        // Q's direct loads (waves 0..3, issued before the metadata fill) are
+        // older than the 2 x 9 register loads just issued
         barrier_keep_seen<2 * kFp8Loads>();
         read_q(buffer(u0 + 2), buffer(u0 + 3));
       } else {
@@ -635,10 +650,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         // resource and the sparse zero token keep such loads in bounds; the
         // buffer is not read), so every path issues the same loads.
         stage_bf16(u0, buffer(u0));
-        stage_q(0, buffer(u0 + 2));
-        stage_q(1, buffer(u0 + 3));
         stage_bf16(u0 + 1, buffer(u0 + 1));
-        // u0 and Q landed; u0 + 1 (5 or 4 loads per wave) stays in flight
+        // u0 and Q (waves 0..3, older) landed; u0 + 1 (5 or 4 loads per wave)
+        // stays in flight
         if (wave_s < 4)
           barrier_keep<kLoads>();
         else
