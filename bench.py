@@ -8,9 +8,12 @@ already resident in HBM: the scheduler kernel (mla_get_metadata) and the decode
 call (mla_decode_with_kvcache: the split-KV decode kernel, then the lse combine
 kernel).  The headline workload is the memory-bound dense BF16 decode (B=64,
 s_q=1, h_q=128, seqlen 4096 for all, block 64, pages a random permutation of
-the pool); it is the one the JSON line reports.  --workloads adds the other
-configurations (dense s_q=2 compute-bound, sparse FP8 top-2048, skewed sparse
-FP8) under "workloads", measured the same way.
+the pool); its step rate is the line's value.  By default the line also
+carries, under "workloads", the compute-bound dense s_q=2 decode (3), the sparse
+FP8 top-2048 decode (4) and the skewed long-context sparse FP8 decode (5),
+measured the same way, each with a roofline of its own: the fraction of the
+HBM peak for the memory-bound ones (2, 5: intensity below the ridge point) and
+of the dense bf16 MFMA peak for the compute-bound ones (3, 4).
 
 Counting (per decode call): FLOPs = 2 (576 + 512) per query row per attended
 token; algorithmic bytes = KV bytes of the attended tokens (1152 B per bf16
@@ -50,7 +53,14 @@ METRIC = "decode TFLOP/s + HBM GB/s vs MI355X roofline; dense bf16 & sparse fp8 
 HEADLINE = 2
 KERNEL_SOURCES = ["mla_paged_kv_get_amd/csrc/mla_decode.hip", "mla_paged_kv_get_amd/csrc/mla_device.hpp",
                   "mla_paged_kv_get_amd/csrc/mla_common.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mla_decode_kernel_dense_bf16_b64_h128_s4096.json")
+# copy-calibrated FETCH_SIZE + WRITE_SIZE summaries of the decode kernel, per workload
+TRAFFIC_FILES = {
+    2: "traffic_mla_decode_kernel_dense_bf16_b64_h128_s4096.json",
+    3: "traffic_mla_decode_kernel_dense_bf16_b128_sq2_h128_varlen.json",
+    4: "traffic_mla_decode_kernel_sparse_fp8_b64_h128_topk2048.json",
+    5: "traffic_mla_decode_kernel_sparse_fp8_skewed_b8_sq2_h64.json",
+}
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
 
 
 def parse():
@@ -58,7 +68,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workloads", default="2", help="comma list of configurations; 2 (the headline) is always run")
+    ap.add_argument("--workloads", default="2,3,4,5",
+                    help="comma list of configurations; 2 (the headline) is always run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--prefill", action="store_true",
@@ -78,11 +89,13 @@ def kernel_source_sha() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the decode kernel on the headline workload, if the
-    committed counter summary was taken on the current kernel sources."""
+def measured_traffic(cfg: int):
+    """HBM bytes per launch of the decode kernel on workload cfg, if the committed
+    counter summary was taken on the current kernel sources."""
+    if cfg not in TRAFFIC_FILES:
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", TRAFFIC_FILES[cfg])) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -157,28 +170,42 @@ def measure(cfg: int, steps: int, warmup: int, calls: bool = True):
     kern = sorted(timer.durations_ms())
     kernel_ms = sum(kern) / len(kern)
 
-    # decode call alone (metadata reused, as across layers): warm, then cold
-    # (1 GiB written between calls, so the KV pool is not served from the MALL)
-    def timed_calls(cold: bool):
-        junk = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if cold else None
-        times = []
+    # decode call alone (metadata reused, as across layers), one call per
+    # iteration: the whole call (decode + combine) by an event pair around it and
+    # the decode kernel alone by the library's events.  Warm: back to back over
+    # the same inputs.  Cold: 1 GiB read between calls (a sum over a scratch
+    # buffer), so neither L2 nor the 256 MB MALL holds the KV pool and no dirty
+    # lines are left to be written back inside the timed call.  cold_write: the
+    # same with 1 GiB written instead (the write-back of those dirty lines then
+    # lands inside the timed call).
+    junk = torch.ones(1 << 28, dtype=torch.float32, device=dev) if calls else None
+
+    def timed_calls(mode: str):
+        calls_ms = []
+        kt = mla.DecodeKernelTimer()
         for _ in range(steps):
-            if cold:
+            if mode == "cold":
+                junk.sum()
+            elif mode == "cold_write":
                 junk.fill_(1)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             hold_gpu(500.0)
             a.record(stream)
-            decode_call(meta)
+            kt.record(lambda: decode_call(meta))
             b.record(stream)
             torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
-        times.sort()
-        return times[len(times) // 2]
+            calls_ms.append(a.elapsed_time(b))
+        kd = sorted(kt.durations_ms())
+        calls_ms.sort()
+        return calls_ms[len(calls_ms) // 2], kd[len(kd) // 2]
 
     # (skipped with --no-calls, so that a kernel trace of the run holds only the
     # warmup and timed steps and its mean decode duration is the one reported)
-    call_warm = timed_calls(False) if calls else float("nan")
-    call_cold = timed_calls(True) if calls else float("nan")
+    nan = (float("nan"), float("nan"))
+    call_warm, kern_warm = timed_calls("warm") if calls else nan
+    call_cold, kern_cold = timed_calls("cold") if calls else nan
+    call_cold_w, kern_cold_w = timed_calls("cold_write") if calls else nan
+    del junk
     # the scheduler kernel alone
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     hold_gpu(100.0 * steps + 2000.0)
@@ -190,12 +217,15 @@ def measure(cfg: int, steps: int, warmup: int, calls: bool = True):
     sched_ms = a.elapsed_time(b) / steps
 
     flops, nbytes = prob.flops(), prob.bytes()
+    us = lambda ms: round(ms * 1e3, 2)
     res = dict(config=cfg, name=prob.name, gen_s=round(gen_s, 2), flops=flops, bytes=nbytes,
-               num_workers=meta.num_workers, splits=meta.total_splits(),
-               step_us=round(step_ms * 1e3, 2), decode_kernel_us=round(kernel_ms * 1e3, 2),
-               decode_kernel_us_median=round(kern[len(kern) // 2] * 1e3, 2),
-               decode_call_us_warm_median=round(call_warm * 1e3, 2),
-               decode_call_us_cold_median=round(call_cold * 1e3, 2), scheduler_us=round(sched_ms * 1e3, 2),
+               intensity=round(flops / nbytes, 1), num_workers=meta.num_workers, splits=meta.total_splits(),
+               step_us=us(step_ms), decode_kernel_us=us(kernel_ms),
+               decode_kernel_us_median=us(kern[len(kern) // 2]),
+               decode_kernel_us_warm_median=us(kern_warm), decode_kernel_us_cold_median=us(kern_cold),
+               decode_kernel_us_cold_write_median=us(kern_cold_w),
+               decode_call_us_warm_median=us(call_warm), decode_call_us_cold_median=us(call_cold),
+               decode_call_us_cold_write_median=us(call_cold_w), scheduler_us=us(sched_ms),
                step_tflops=round(flops / (step_ms * 1e-3) / 1e12, 2),
                kernel_tflops=round(flops / (kernel_ms * 1e-3) / 1e12, 2),
                kernel_gbps=round(nbytes / (kernel_ms * 1e-3) / 1e9, 1),
@@ -206,6 +236,15 @@ def measure(cfg: int, steps: int, warmup: int, calls: bool = True):
             res[k] = None
     res["kernel_frac_hbm"] = round(res["kernel_gbps"] / PEAK_HBM_GBS, 4)
     res["kernel_frac_mfma"] = round(res["kernel_tflops"] / PEAK_BF16_TFLOPS, 4)
+    # the roofline this workload sits under: HBM below the ridge point, MFMA above
+    mem_bound = flops / nbytes < RIDGE
+    res["roofline"] = dict(
+        bound="hbm" if mem_bound else "mfma",
+        achieved=res["kernel_gbps"] if mem_bound else res["kernel_tflops"],
+        peak=PEAK_HBM_GBS if mem_bound else PEAK_BF16_TFLOPS, unit="GB/s" if mem_bound else "TFLOP/s",
+        frac=res["kernel_frac_hbm"] if mem_bound else res["kernel_frac_mfma"],
+        traffic=measured_traffic(cfg),
+        per_launch=dict(algorithmic_bytes=nbytes, flops=flops, kernel_us=res["decode_kernel_us"]))
     if calls and topk == 0 and prob.s_q > 1:
         # speculative query tokens with the causal mask (query token s of s_q sees
         # positions <= seqlen - s_q + s): the same decode kernel, timed the same way
@@ -235,13 +274,23 @@ def cpu_baseline(prob):
     import oracle
 
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     t0 = time.perf_counter()
     oracle.problem_decode(prob, None)
     dt = time.perf_counter() - t0
     return dict(value=round(prob.flops() / dt / 1e12, 5), unit="TFLOP/s", cores=threads, kind="oracle",
                 sample="all %d query rows of the headline workload (%.1f GFLOP, %.1f MB algorithmic), %.1f s" % (
                     prob.B * prob.s_q * prob.h_q, prob.flops() / 1e9, prob.bytes() / 1e6, dt),
-                seconds=round(dt, 2), gbps=round(prob.bytes() / dt / 1e9, 3))
+                seconds=round(dt, 2), gbps=round(prob.bytes() / dt / 1e9, 3), cpu_model=cpu_model,
+                host_cpus=os.cpu_count())
 
 
 PREFILL_SHAPE = dict(s_q=2048, h_q=128, s_kv=8192, topk=2048, n_invalid=102)
@@ -309,9 +358,12 @@ def main():
     for c in cfgs:
         prob, r = measure(c, args.steps, args.warmup, calls=not args.no_calls)
         results[c] = r
-        print("[bench] config %d %s: step %.1f us, decode kernel %.1f us (%.1f TFLOP/s, %.0f GB/s), call warm %s us, "
-              "cold %s us, scheduler %.1f us, W=%d, %d splits" % (
+        print("[bench] config %d %s: step %.1f us, decode kernel %.1f us (%.1f TFLOP/s, %.0f GB/s, %.1f %% of the %s "
+              "roofline); kernel warm / cold / cold-after-writes %s / %s / %s us; call warm / cold %s / %s us; "
+              "scheduler %.1f us, W=%d, %d splits" % (
                   c, prob.name, r["step_us"], r["decode_kernel_us"], r["kernel_tflops"], r["kernel_gbps"],
+                  100 * r["roofline"]["frac"], r["roofline"]["bound"], r["decode_kernel_us_warm_median"],
+                  r["decode_kernel_us_cold_median"], r["decode_kernel_us_cold_write_median"],
                   r["decode_call_us_warm_median"], r["decode_call_us_cold_median"], r["scheduler_us"],
                   r["num_workers"], r["splits"]), file=sys.stderr, flush=True)
         if "causal_decode_kernel_us" in r:
@@ -320,10 +372,10 @@ def main():
         if c == head:
             head_prob = prob
     h = results[head]
-    roofline = dict(bound="hbm", achieved=h["kernel_gbps"], peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=h["kernel_frac_hbm"], traffic=measured_traffic() if head == HEADLINE else None,
-                    kernel="mla_decode_kernel (split-KV decode), mean of per-launch HIP events over the timed steps",
-                    mfma_frac=h["kernel_frac_mfma"])
+    roofline = dict(h["roofline"])
+    roofline.pop("per_launch")
+    roofline.update(kernel="mla_decode_kernel (split-KV decode), mean of per-launch HIP events over the timed steps",
+                    hbm_frac=h["kernel_frac_hbm"], mfma_frac=h["kernel_frac_mfma"])
     line = dict(metric=METRIC, value=h["step_tflops"], unit="TFLOP/s", n_gpus=1, steps=args.steps,
                 warmup=args.warmup, ms_per_step=round(h["step_us"] / 1e3, 5), higher_is_better=True, scaling="weak",
                 vs_baseline=None, dtype="bf16", data="synthetic",

@@ -270,8 +270,9 @@ class DecodeKernelTimer:
 
     def _event(self):
         ev = ctypes.c_void_p()
-        if self._hip.hipEventCreateWithFlags(ctypes.byref(ev), self._DISABLE_SYSTEM_FENCE) != 0:
-            raise MlaError("hipEventCreateWithFlags failed")
+        rc = self._hip.hipEventCreateWithFlags(ctypes.byref(ev), self._DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise MlaError(-4, "hipEventCreateWithFlags", "hipError_t %d" % rc)
         return ev
 
     def record(self, fn):
@@ -286,11 +287,13 @@ class DecodeKernelTimer:
     def durations_ms(self):
         out = []
         for a, b in self._pairs:
-            if self._hip.hipEventSynchronize(b) != 0:
-                raise MlaError("hipEventSynchronize failed")
+            rc = self._hip.hipEventSynchronize(b)
+            if rc != 0:
+                raise MlaError(-4, "hipEventSynchronize", "hipError_t %d" % rc)
             ms = ctypes.c_float()
-            if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
-                raise MlaError("hipEventElapsedTime failed")
+            rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+            if rc != 0:
+                raise MlaError(-4, "hipEventElapsedTime", "hipError_t %d" % rc)
             out.append(ms.value)
         for a, b in self._pairs:
             self._hip.hipEventDestroy(a)

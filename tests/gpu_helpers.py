@@ -45,8 +45,15 @@ def flat(o, lse):
     return o, lse
 
 
+def record_margin(what, do, ratio, dl):
+    """Keep a case's margins for the terminal summary (conftest.MARGINS)."""
+    import conftest
+
+    conftest.MARGINS.append((what, float(do), float(ratio), float(dl)))
+
+
 def compare(o, lse, o_ref, lse_ref, what=""):
-    """Assert the tolerance; returns (max |d o|, max |d lse|)."""
+    """Assert the tolerance; returns (max |d o|, max |d lse|) and records them."""
     empty = np.isneginf(lse_ref)
     assert np.all(np.isneginf(lse[empty])), "%s: rows with no attended token must give lse = -inf" % what
     assert np.all(o[empty] == 0.0), "%s: rows with no attended token must give o = 0" % what
@@ -58,7 +65,10 @@ def compare(o, lse, o_ref, lse_ref, what=""):
     assert not bad.any(), "%s: %d/%d o elements out of tolerance, worst |d| %.3g" % (what, bad.sum(), bad.size, do.max())
     dl = np.abs(lse[live] - lse_ref[live])
     assert np.all(dl <= LSE_ATOL), "%s: lse out of tolerance, worst |d| %.3g" % (what, dl.max())
-    return (float(do.max()) if do.size else 0.0), (float(dl.max()) if dl.size else 0.0)
+    do_max = float(do.max()) if do.size else 0.0
+    dl_max = float(dl.max()) if dl.size else 0.0
+    record_margin(what, do_max, float((do / bound).max()) if do.size else 0.0, dl_max)
+    return do_max, dl_max
 
 
 def check_problem(prob, rows=None, num_workers=0, what=None, causal=False):
