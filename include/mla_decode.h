@@ -136,6 +136,31 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
                                     float* lse, void* stream);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The same computation, arguments and errors as
+ * mla_decode_with_kvcache, without the workspace arguments: the split workspace
+ * (partial outputs and their lse) lives in a static device array of
+ * MLA_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held until the
+ * process ends.  The caller still passes the inputs, the metadata and o / lse.
+ * Shapes whose workspace (mla_get_metadata_size's workspace_bytes) exceeds
+ * MLA_NOALLOC_SCRATCH_BYTES are refused with MLA_ERR_UNSUPPORTED before any
+ * launch.  The call never allocates: the array's device address is looked up
+ * (hipGetSymbolAddress) on the first call on each device and kept.  Every call
+ * on one GPU shares that GPU's array, so calls that overlap in time on one GPU
+ * (concurrent streams, several host threads) race and give wrong results;
+ * calls ordered on one stream are safe.  Nothing in the array needs clearing
+ * between calls: each call writes every workspace entry it reads.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+MLA_API int mla_decode_with_kvcache_noalloc(const void* q, const void* kvcache, int64_t num_blocks,
+                                            const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                                            int B, int s_q, int h_q, int h_kv, int d_qk, int d_v, float softmax_scale,
+                                            const int32_t* metadata, size_t metadata_bytes, int num_workers,
+                                            const int32_t* indices, int topk, int is_fp8, int causal, void* o,
+                                            float* lse, void* stream);
+
+/*
  * Sparse prefill: token-sparse attention of many query tokens over one
  * contiguous latent KV sequence ("FlashMLA" summary on agentlenshq.com, usage
  * section, the sparse prefill call flash_mla_sparse_fwd(q, kv, indices, ...):

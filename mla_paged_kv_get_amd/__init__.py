@@ -7,8 +7,10 @@ thin ctypes binding with the same function names.  mla_sparse_prefill runs
 the sparse path over one contiguous KV sequence (many query tokens, each with
 its own index list).
 """
-from .binding import (DecodeKernelTimer, Metadata, MlaError, mla_debug_dequant_fp8, mla_decode_with_kvcache, mla_get_metadata,
+from .binding import (DecodeKernelTimer, Metadata, MlaError, mla_debug_dequant_fp8, mla_decode_with_kvcache,
+                      mla_decode_with_kvcache_noalloc, mla_get_metadata,
                       mla_get_metadata_size, mla_last_error, mla_sparse_prefill, lib, LIB_PATH)
 
-__all__ = ["DecodeKernelTimer", "Metadata", "MlaError", "mla_debug_dequant_fp8", "mla_decode_with_kvcache", "mla_get_metadata",
+__all__ = ["DecodeKernelTimer", "Metadata", "MlaError", "mla_debug_dequant_fp8", "mla_decode_with_kvcache",
+           "mla_decode_with_kvcache_noalloc", "mla_get_metadata",
            "mla_get_metadata_size", "mla_last_error", "mla_sparse_prefill", "lib", "LIB_PATH"]

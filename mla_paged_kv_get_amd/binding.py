@@ -55,6 +55,9 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_with_kvcache.restype = I
         L.mla_decode_with_kvcache.argtypes = [P, P, I64, P, I, P, I, I, I, I, I, I, ctypes.c_float, P, Z, I, P, I, I, I,
                                               P, Z, P, P, P]
+        L.mla_decode_with_kvcache_noalloc.restype = I
+        L.mla_decode_with_kvcache_noalloc.argtypes = [P, P, I64, P, I, P, I, I, I, I, I, I, ctypes.c_float, P, Z, I, P,
+                                                      I, I, I, P, P, P]
         L.mla_sparse_prefill_workspace_size.restype = I
         L.mla_sparse_prefill_workspace_size.argtypes = [I, I, I, I64, I, I, ctypes.POINTER(Z), ctypes.POINTER(I)]
         L.mla_sparse_prefill.restype = I
@@ -190,6 +193,38 @@ def mla_decode_with_kvcache(q: torch.Tensor, kvcache: torch.Tensor, block_table:
             topk, int(is_fp8), int(bool(causal)), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _ptr(out), _ptr(lse), _stream(dev)), "mla_decode_with_kvcache")
     return out, lse
+
+
+def mla_decode_with_kvcache_noalloc(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor,
+                                    cache_seqlens: torch.Tensor, d_v: int, metadata: Metadata, out: torch.Tensor,
+                                    lse: torch.Tensor, indices: Optional[torch.Tensor] = None, is_fp8: bool = False,
+                                    softmax_scale: Optional[float] = None, causal: bool = False) -> None:
+    """mla_decode_with_kvcache without a workspace argument: the library's static
+    scratch holds the split workspace, and the caller passes o (bf16
+    [B, s_q, h_q, 512]) and lse (fp32 [B, s_q, h_q]), so nothing is allocated."""
+    dev = q.device
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[3] != D_QK:
+        raise ValueError("q must be bf16 [B, s_q, h_q, 576]")
+    B, s_q, h_q = (int(x) for x in q.shape[:3])
+    for name, t in (("q", q), ("kvcache", kvcache), ("block_table", block_table), ("cache_seqlens", cache_seqlens),
+                    ("out", out), ("lse", lse)) + ((("indices", indices),) if indices is not None else ()):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("%s must be contiguous and on %s" % (name, dev))
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, s_q, h_q, D_V):
+        raise ValueError("out must be bf16 [B, s_q, h_q, 512]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, s_q, h_q):
+        raise ValueError("lse must be fp32 [B, s_q, h_q]")
+    topk = 0 if indices is None else int(indices.shape[2])
+    m = metadata
+    if (m.B, m.s_q, m.h_q, m.topk) != (B, s_q, h_q, topk):
+        raise ValueError("metadata was built for another shape")
+    scale = float(softmax_scale) if softmax_scale is not None else 1.0 / math.sqrt(D_QK)
+    with torch.cuda.device(dev):
+        _check(lib().mla_decode_with_kvcache_noalloc(
+            _ptr(q), _ptr(kvcache), int(kvcache.shape[0]), _ptr(block_table), int(block_table.shape[1]),
+            _ptr(cache_seqlens), B, s_q, h_q, m.h_kv, D_QK, d_v, scale, _ptr(m.tensor), m.tensor.numel() * 4,
+            m.num_workers, _ptr(indices), topk, int(is_fp8), int(bool(causal)), _ptr(out), _ptr(lse), _stream(dev)),
+            "mla_decode_with_kvcache_noalloc")
 
 
 def mla_sparse_prefill(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,

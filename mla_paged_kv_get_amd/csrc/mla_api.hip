@@ -125,6 +125,32 @@ int prefill_layout(int s_q, int h_q, int h_kv, int64_t s_kv, int topk, int num_w
   return MLA_OK;
 }
 
+// Scratch of mla_decode_with_kvcache_noalloc: the split workspace (partial
+// outputs and their lse) in a static device array, for callers that cannot
+// allocate.  In host code `scratch` is only a stand-in for the symbol; its
+// device address (one copy per GPU) comes from hipGetSymbolAddress, taken once
+// per device on the entry point's first call there and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MLA_ERR_UNSUPPORTED, "device ordinal %d beyond 63", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -238,6 +264,32 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
   e = mla::launch_combine(p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return MLA_OK;
+}
+
+MLA_API int mla_decode_with_kvcache_noalloc(const void* q, const void* kvcache, int64_t num_blocks,
+                                            const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                                            int B, int s_q, int h_q, int h_kv, int d_qk, int d_v, float softmax_scale,
+                                            const int32_t* metadata, size_t metadata_bytes, int num_workers,
+                                            const int32_t* indices, int topk, int is_fp8, int causal, void* o,
+                                            float* lse, void* stream) {
+  g_err[0] = 0;
+  Shape s;
+  int rc = shape_of(B, s_q, h_q, h_kv, topk, &s);
+  if (rc != MLA_OK) return rc;
+  int W = 0;
+  rc = resolve_workers(num_workers, s, &W);
+  if (rc != MLA_OK) return rc;
+  size_t meta, part_o, ws;
+  sizes(s, W, &meta, &part_o, &ws);
+  if (ws > kScratchBytes)
+    return fail(MLA_ERR_UNSUPPORTED, "this shape needs %zu bytes of split workspace; the static scratch holds %zu", ws,
+                kScratchBytes);
+  void* ptr = nullptr;
+  rc = scratch_address(&ptr);
+  if (rc != MLA_OK) return rc;
+  return mla_decode_with_kvcache(q, kvcache, num_blocks, block_table, max_blocks, cache_seqlens, B, s_q, h_q, h_kv,
+                                 d_qk, d_v, softmax_scale, metadata, metadata_bytes, W, indices, topk, is_fp8, causal,
+                                 ptr, kScratchBytes, o, lse, stream);
 }
 
 MLA_API int mla_set_decode_kernel_events(void* start, void* stop) {

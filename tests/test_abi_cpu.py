@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     syms = declared_symbols()
     assert set(syms) == {"mla_get_metadata_size", "mla_get_metadata", "mla_decode_with_kvcache", "mla_last_error",
                          "mla_debug_dequant_fp8", "mla_set_decode_kernel_events",
-                         "mla_sparse_prefill_workspace_size", "mla_sparse_prefill"}
+                         "mla_sparse_prefill_workspace_size", "mla_sparse_prefill",
+                         "mla_decode_with_kvcache_noalloc"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -152,3 +153,16 @@ def test_sparse_prefill_workspace_size(L):
         kw.update(bad)
         rc, _, _ = prefill_size(L, **kw)
         assert rc < 0, bad
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(L):
+    """The allocation-free entry point checks the shape's workspace against its
+    static scratch on the host and refuses larger ones before any HIP call."""
+    f = L.mla_decode_with_kvcache_noalloc
+    f.argtypes = None
+    P = ctypes.c_void_p
+    # 4096 requests x 512 query rows: the split workspace is far beyond 128 MiB
+    rc = f(P(0x1000), P(0x2000), ctypes.c_int64(4), P(0x3000), 4, P(0x4000), 4096, 4, 128, 1, 576, 512,
+           ctypes.c_float(0.0), P(0x5000), ctypes.c_size_t(1 << 30), 256, None, 0, 0, 0, P(0x7000), P(0x8000), None)
+    assert rc == -2
+    assert "scratch" in L.mla_last_error().decode()
