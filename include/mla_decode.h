@@ -85,8 +85,10 @@ MLA_API int mla_get_metadata_size(int B, int s_q, int h_q, int h_kv, int topk, i
  * Scheduler: spreads the (request, KV tile range) work of a decode step over
  * num_workers workers (one launch of a single-workgroup kernel on `stream`).
  *   cache_seqlens  device int32 [B], tokens cached per request (>= 0)
- *   is_fp8         1 if the cache will be the 656-byte FP8 layout (tunes the
- *                  smallest split), else 0
+ *   is_fp8         1 if the cache will be the 656-byte FP8 layout, else 0 (checked
+ *                  to be 0 or 1; the split rule is the same for both caches: on
+ *                  every measured workload the finest balanced split, one
+ *                  workgroup per compute unit, was fastest, also for FP8)
  *   metadata       device buffer of metadata_bytes (>= the size call's value);
  *                  written entirely by the kernel
  * The metadata stays valid for every layer's decode call while cache_seqlens,
