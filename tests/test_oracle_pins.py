@@ -348,6 +348,59 @@ def test_fp8_equals_bf16_on_representable_data():
     assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
 
 
+def exact_product_attention(prob):
+    """o, lse of the FP8 problem with each element read as the exact product
+    e4m3fn(code) x scale in float64 (no rounding to fp32 or bf16), via torch
+    SDPA / logsumexp in float64: the other reading of the dequantisation."""
+    kv = prob.kvcache.reshape(-1, mi.FP8_TOKEN_BYTES)
+    vals = kv[:, :512].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
+    scales = kv[:, 512:528].contiguous().view(torch.float32).to(torch.float64)
+    rope = kv[:, 528:].contiguous().view(torch.bfloat16).to(torch.float64)
+    K_all = torch.cat([vals * scales.repeat_interleave(128, dim=1), rope], dim=1)
+    o = np.full((prob.B * prob.s_q * prob.h_q, 512), np.nan)
+    lse = np.full(prob.B * prob.s_q * prob.h_q, np.nan)
+    for b in range(prob.B):
+        for s in range(prob.s_q):
+            pos = prob.indices[b, s].to(torch.int64)
+            pos = pos[pos != -1]
+            phys = prob.block_table[b].to(torch.int64)[pos // 64] * 64 + pos % 64
+            K = K_all[phys]
+            q = prob.q[b, s].to(torch.float64)
+            r = (b * prob.s_q + s) * prob.h_q
+            o[r:r + prob.h_q] = F.scaled_dot_product_attention(
+                q[None, None], K[None, None], K[None, None, :, :512].contiguous(), scale=prob.softmax_scale)[0, 0].numpy()
+            lse[r:r + prob.h_q] = torch.logsumexp(prob.softmax_scale * (q @ K.T), dim=-1).numpy()
+    return o, lse
+
+
+@pytest.mark.parametrize("recipe", ["c4", "c5"])
+def test_fp8_bf16_reading_within_tolerance_of_exact_product(recipe):
+    """The oracle reads an FP8 element as bf16(fp32(code x scale)) (the kernel
+    turns the values back into bf16 before its bf16 multiply); the exact product
+    code x scale is the other plain reading.  On inputs made like the sparse FP8
+    workloads (random latents quantised per 128-dim tile, index lists with -1
+    slots) the two readings differ by a small part of the parity tolerance
+    (measured: o by 5-7 % of its bound, lse by 1.6e-4-2.6e-4 against 1e-3), so
+    the choice between them cannot decide a parity result."""
+    if recipe == "c4":
+        prob = mi.make_problem("fp8 reading", 3, 1, 128, [32768, 20000, 5000], seed=501, topk=2048, is_fp8=True,
+                               n_invalid=102)
+    else:
+        prob = mi.make_problem("fp8 reading", 2, 2, 64, [8192, 1024], seed=502, topk=2048, is_fp8=True,
+                               n_invalid=0, recipe="clip")
+    o_b, l_b = oracle.problem_decode(prob)
+    o_x, l_x = exact_product_attention(prob)
+    do = np.abs(o_b - o_x)
+    ratio = (do / (8e-3 + 1e-2 * np.abs(o_x))).max()
+    dl = np.abs(l_b - l_x).max()
+    # the bf16 step moves each element by at most 2^-9 of itself, and a score
+    # (a sum over 576 products) by less; o and lse stay well inside
+    # |d o| <= 8e-3 + 1e-2 |o| and |d lse| <= 1e-3
+    assert ratio < 0.1, ratio
+    assert dl < 0.5e-3, dl
+    assert do.max() > 0.0  # the readings do differ: the bf16 step is not a no-op here
+
+
 @pytest.mark.parametrize("is_fp8,topk", [(False, 0), (True, 96)])
 def test_unattended_tokens_are_never_read(is_fp8, topk):
     kw = dict(B=2, s_q=1, h_q=3, seqlens=[130, 70], seed=101, is_fp8=is_fp8, topk=topk, n_spare=2, max_blocks=4)
