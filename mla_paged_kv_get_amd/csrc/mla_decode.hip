@@ -15,10 +15,11 @@
 // sustain, and each wave's waits (LDS, barrier) are covered by the other's MFMAs.
 // Per 32-token sub-tile of the KV stream:
 //   1. the sub-tile's bf16 rows are staged in a swizzled LDS tile (BF16: direct
-//      global->LDS 16-byte loads; FP8: 16-byte loads into VGPRs, e4m3 -> fp32
-//      (exact) * scale (RNE) -> bf16 (RNE), then LDS); four buffers hold the
-//      sub-tile being multiplied by V, the next one (whose scores are being
-//      computed) and the two behind it;
+//      global->LDS 16-byte loads, three sub-tiles ahead; FP8: 8-byte code
+//      loads into VGPRs a round before their store, e4m3 -> fp32 (exact) *
+//      scale (RNE) -> bf16 (RNE), then LDS); four buffers hold the sub-tile
+//      being multiplied by V, the next one (whose scores are being computed)
+//      and the two behind it;
 //   2. scores: wave w computes S^T for 16 query rows (16 (w & 3) ..) and 16 tokens
 //      (16 (w >> 2) ..) over all 576 dims on v_mfma_f32_16x16x32_bf16, with its Q
 //      rows in VGPRs, so no wave needs another's partial scores;
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       }
     };
     // FP8 metadata goes through VGPRs instead (its tile loads are VGPR loads,
-    // two rounds in flight, and the compiler counts register loads exactly):
+    // and the compiler counts register loads exactly):
     // every wave loads, in round u before that round's tile loads, the indices of
     // sub-tile u + 8 and the pages of sub-tile u + 6 (dense: its page), and wave 0
     // writes them into the rings in round u + 1, right after the store that waits
@@ -607,7 +608,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     float m_ref = kNegInf, m_seen = kNegInf, l_sum = 0.f;
     bool redo = false;
     int pass = 0;  // at most two: the second pass runs with the split's row maximum
-    constexpr int kAhead = FP8 ? (SPARSE ? 2 : 3) : 4;  // K fragments read ahead of their score MFMA
+    // K fragments read ahead of their score MFMA.  FP8 holds one sub-tile in
+    // VGPRs between its load and its store (loaded one round ahead): a second
+    // set (two rounds ahead) left registers for only two or three fragments
+    // ahead, and the reads' LDS latency then cost more than the lead gained
+    // (c4 -4..-6 us with one set and four fragments).
+    constexpr int kAhead = 4;
     constexpr bool kPreK = !FP8;           // the first ones read before the round's barrier
     constexpr int kPRead = FP8 ? 16 : 13;  // score MFMA after which the P fragments are read
     do {
@@ -618,11 +624,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       // Q goes through the buffers of sub-tiles u0 + 2 and u0 + 3 before they
       // hold tiles.  BF16: sub-tiles u0 and u0 + 1 and Q issued; u0 and Q landed;
       // Q read; then u0 + 2 issued into its buffer.  FP8: u0 and u0 + 1 loaded and
-      // stored, Q landed and read, u0 + 2 and u0 + 3 in flight in VGPRs.  Then S
+      // stored, Q landed and read, u0 + 2 in flight in VGPRs.  Then S
       // of u0 and the reference, whose barrier ends every wave's reads of Q
       // before round u0 stores sub-tile u0 + 2 there.
-      RawFp8 raw[2];       // FP8: sub-tile x in VGPRs (set (x - u0) & 1) until its store
-      Fp8Meta fmeta[2];    // FP8: metadata loaded in a round of each set, written next round
+      RawFp8 raw[2];       // FP8: a sub-tile in VGPRs between its load and its store (raw[1]: prologue only)
+      Fp8Meta fmeta[2];    // FP8: metadata loaded in a round, written the next (alternating sets)
       if constexpr (FP8) {
         meta_fill();
         if constexpr (SPARSE) {
@@ -639,10 +645,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         store_fp8(raw[0], buffer(u0));
         store_fp8(raw[1], buffer(u0 + 1));
         load_fp8(u0 + 2, raw[0], fp8_rows(u0 + 2));
-        load_fp8(u0 + 3, raw[1], fp8_rows(u0 + 3));
         // Q's direct loads (waves 0..3, issued before the metadata fill) are
-        // older than the 2 x 9 register loads just issued
-        barrier_keep_seen<2 * kFp8Loads>();
+        // older than the 9 register loads just issued
+        barrier_keep_seen<kFp8Loads>();
         read_q(buffer(u0 + 2), buffer(u0 + 3));
       } else {
         meta_fill();
@@ -708,8 +713,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       // in s (round u0: from the prologue), the first K fragments of sub-tile u in
       // kf, V^T of sub-tile u - 1 in va and P of sub-tile u - 1 in LDS:
       //   scores of sub-tile u (round u0: computed already), with the staging of a
-      //   later sub-tile (BF16: direct loads of u + 3; FP8: store of u + 2, loads
-      //   of u + 3) between the MFMAs;
+      //   later sub-tile (BF16: direct loads of u + 3; FP8: store of u + 2, then
+      //   its registers reloaded with u + 3) between the MFMAs;
       //   O += P V of sub-tile u - 1, with the softmax of sub-tile u, its P write
       //   and the V^T reads of sub-tile u between the MFMAs;
       //   the first K fragments of sub-tile u + 1; one barrier.
@@ -730,14 +735,14 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         // round after u0, whose sub-tile was still landing when round u0 ended)
         constexpr bool kSelfK = decltype(kself_tag)::value != 0;
         constexpr int kIssue = decltype(issue_tag)::value;
-        constexpr int kSet = decltype(set_tag)::value;  // FP8: the VGPR set this round stores and refills
+        constexpr int kSet = decltype(set_tag)::value;  // FP8: the metadata set this round loads
         const bool issue = kIssue == 1 || u + 3 < u1;  // sub-tile u + 3 exists (workgroup-uniform)
         __builtin_amdgcn_sched_barrier(0);
-        // FP8 dense: the page of sub-tile u + 4, read before this round's K
+        // FP8 dense: the page of sub-tile u + 3, read before this round's K
         // fragments (sparse: its four token rows are read at the load; holding
         // them across the first score MFMAs costs the registers it lacks)
         Fp8Rows nrows;
-        if constexpr (FP8 && !SPARSE) nrows = fp8_rows(u + 4);
+        if constexpr (FP8 && !SPARSE) nrows = fp8_rows(u + 3);
         // staging work placed after score MFMA kk
         auto stage_step = [&](int kk) __attribute__((always_inline)) {
           if constexpr (FP8) {
@@ -745,15 +750,15 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
             // (past the split they read in-bounds bytes that are never used), so
             // that the compiler's wait for them is a count on every path.
             if (kk == 1) {
-              store_fp8(raw[kSet], nxt);  // sub-tile u + 2, loaded two rounds ago
+              store_fp8(raw[0], nxt);  // sub-tile u + 2, loaded in the previous round
               if (!kFirst) fp8_meta_publish(u - 1, fmeta[kSet ^ 1]);
             }
             if (kk == 2) fmeta[kSet] = fp8_meta_load(u);
             if (kk == 3) {
               if constexpr (SPARSE)
-                load_fp8(u + 4, raw[kSet], fp8_rows(u + 4));
+                load_fp8(u + 3, raw[0], fp8_rows(u + 3));
               else
-                load_fp8(u + 4, raw[kSet], nrows);
+                load_fp8(u + 3, raw[0], nrows);
             }
           } else {
             if (issue) {
@@ -843,7 +848,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       round(Tag<1>{}, Tag<-1>{}, Tag<0>{}, Tag<0>{}, u0, buffer(u0), buffer(u0 + 1), buffer(u0 + kStageAhead));
       int u = u0 + 1;
       if constexpr (FP8) {
-        // unrolled by two: round u stores and refills VGPR set (u - u0) & 1
+        // unrolled by two: the metadata sets alternate between rounds
         for (; u + 1 < u1; u += 2) {
           round(Tag<0>{}, Tag<-1>{}, Tag<1>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
           round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, Tag<1>{}, u + 1, buffer(u + 1), buffer(u + 2),
