@@ -131,6 +131,33 @@ def test_forced_worker_counts(W):
     check_problem(sp, num_workers=W, what="sparse fp8 W=%d" % W)
 
 
+@pytest.mark.parametrize("is_fp8,topk,W", [(False, 0, 256), (True, 0, 96), (False, 4096, 256), (True, 4096, 64)],
+                         ids=["dense bf16 W=256", "dense fp8 W=96", "sparse bf16 W=256", "sparse fp8 W=64"])
+def test_many_splits_per_stream(is_fp8, topk, W):
+    """Long streams cut into 32-64 splits: the combine kernel's path for more
+    splits than it loads at once (lse values first, then the split outputs
+    eight at a time), next to a short stream (dense) or a second long one
+    (sparse); the combine variant that loads 16 splits at once."""
+    prob = mi.make_problem("many splits", 2, 1, 32, [8192, 100], seed=130 + W, topk=topk, is_fp8=is_fp8,
+                           n_invalid=40 if topk else 0, recipe="clip")
+    import mla_paged_kv_get_amd as mla
+
+    m = mla.mla_get_metadata(prob.cache_seqlens.to(DEV), 1, 32, 1, topk, is_fp8, W)
+    mm = m.tensor.cpu().numpy()
+    n = np.diff(mm[16 + 8 * W:16 + 8 * W + 3])
+    say("[gpu] many splits W=%d: splits per stream %s" % (W, list(n)))
+    assert n.max() > 16
+    check_problem(prob, num_workers=W, what="many splits %s topk=%d W=%d" % ("fp8" if is_fp8 else "bf16", topk, W))
+
+
+def test_many_splits_among_short_streams():
+    """One 8192-token stream among fifteen one-tile streams, 128 workers: the
+    combine variant that loads 8 splits at once takes its looping path for the
+    long stream's 64 splits."""
+    prob = mi.make_problem("many splits among short", 16, 1, 32, [8192] + [64] * 15, seed=141)
+    check_problem(prob, num_workers=128, what="64 splits among one-split streams")
+
+
 @pytest.mark.parametrize("is_fp8,topk", [(False, 0), (True, 0), (False, 320), (True, 320)],
                          ids=["dense bf16", "dense fp8", "sparse bf16", "sparse fp8"])
 @pytest.mark.parametrize("W", [5, 19, 61, 150])
