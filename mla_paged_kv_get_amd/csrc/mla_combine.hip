@@ -11,6 +11,8 @@
 // at a time, so a workgroup pays one memory round trip per eight splits instead
 // of one per row it visits.  With at most sixteen splits the lse values and
 // the split outputs are loaded together: one round trip in all.
+#include <algorithm>
+
 #include "mla_common.hpp"
 
 namespace mla {
@@ -20,18 +22,9 @@ namespace {
 constexpr int kCombineThreads = 256;  // four rows x 64 threads (8 columns each)
 constexpr int kCombineBatch = 8;  // split outputs in flight per thread
 
-// kCombineFused: up to this many splits, the lse values and the outputs are
-// loaded together (8 or 16; the wider variant holds more VGPRs, so fewer waves
-// fit on a CU, and the host uses it only when streams have many splits).
+// One thread's 8 columns of one row of the stream.
 template <int kCombineFused>
-__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodeParams p) {
-  const int stream = blockIdx.x;
-  const int32_t* split_off = p.meta + meta_split_offset(p.W);
-  const int s0 = split_off[stream];
-  const int n = split_off[stream + 1] - s0;
-  if (n == 1) return;  // finished by the decode kernel
-  const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (row >= p.R_stream) return;
+__device__ __forceinline__ void combine_row(const DecodeParams& p, int stream, int s0, int n, int row) {
   const int c = (threadIdx.x & 63) * 8;
   const int64_t row_base = (int64_t)stream * p.R_stream;
   constexpr float kNegInf = -__builtin_huge_valf();
@@ -134,15 +127,52 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodePara
   write_out(acc, acc2, L);
 }
 
+// kCombineFused: up to this many splits, the lse values and the outputs are
+// loaded together (8 or 16; the wider variant holds more VGPRs, so fewer waves
+// fit on a CU, and the host uses it only when streams have many splits).
+// kLoop: the grid is capped and each workgroup takes several groups of rows.
+template <int kCombineFused, bool kLoop>
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(DecodeParams p) {
+  const int stream = blockIdx.x;
+  const int32_t* split_off = p.meta + meta_split_offset(p.W);
+  const int s0 = split_off[stream];
+  const int n = split_off[stream + 1] - s0;
+  if (n == 1) return;  // finished by the decode kernel
+  if constexpr (kLoop) {
+    // a capped grid: this workgroup's share of the stream's groups of 4 rows
+    const int groups = (p.R_stream + 3) / 4;
+    const int per = (groups + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int g1 = min(groups, ((int)blockIdx.y + 1) * per);
+    for (int g = (int)blockIdx.y * per; g < g1; ++g) {
+      const int row = g * 4 + (threadIdx.x >> 6);
+      if (row < p.R_stream) combine_row<kCombineFused>(p, stream, s0, n, row);
+    }
+  } else {
+    const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (row < p.R_stream) combine_row<kCombineFused>(p, stream, s0, n, row);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.n_streams, (p.R_stream + 3) / 4);
+  // One workgroup per (stream, 4 rows), unless that is more than eight passes of
+  // the chip (many streams, e.g. sparse prefill, most with one split and their
+  // workgroups returning at once): then about 2048 workgroups, each looping
+  // over up to four of a stream's row groups (prefill combine 15.9 -> 5.6 us;
+  // with few streams the loop measured slower, so it is not used there).
+  const int groups = (p.R_stream + 3) / 4;
+  const bool cap = (int64_t)p.n_streams * groups > 16384;
+  const int gy = cap ? std::max((groups + 3) / 4, std::min(groups, (2048 + p.n_streams - 1) / p.n_streams)) : groups;
+  const dim3 grid(p.n_streams, gy);
   // more than 8 workers per stream: streams are likely cut into more than 8 splits
-  if (p.W > 8 * p.n_streams)
-    hipLaunchKernelGGL(mla_combine_kernel<16>, grid, dim3(kCombineThreads), 0, stream, p);
+  const bool wide = p.W > 8 * p.n_streams;
+  if (wide)
+    hipLaunchKernelGGL((cap ? mla_combine_kernel<16, true> : mla_combine_kernel<16, false>), grid,
+                       dim3(kCombineThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(mla_combine_kernel<8>, grid, dim3(kCombineThreads), 0, stream, p);
+    hipLaunchKernelGGL((cap ? mla_combine_kernel<8, true> : mla_combine_kernel<8, false>), grid,
+                       dim3(kCombineThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -150,6 +150,29 @@ def test_many_splits_per_stream(is_fp8, topk, W):
     check_problem(prob, num_workers=W, what="many splits %s topk=%d W=%d" % ("fp8" if is_fp8 else "bf16", topk, W))
 
 
+def test_combine_over_many_streams():
+    """2048 sparse streams of 64 rows (more than 8 passes of the chip at one
+    workgroup per 4 rows): the combine kernel's capped grid, each workgroup
+    looping over several row groups; 250 workers put split points inside
+    streams, so some streams are merged while most are finished by the decode
+    kernel.  Checked on a seeded sample of rows that includes every row of the
+    merged streams."""
+    import mla_paged_kv_get_amd as mla
+
+    prob = mi.make_problem("many streams", 1024, 2, 64, [200] * 1024, seed=151, topk=128, n_invalid=3,
+                           recipe="clip")
+    m = mla.mla_get_metadata(prob.cache_seqlens.to(DEV), 2, 64, 1, 128, False, 250)
+    mm = m.tensor.cpu().numpy()
+    n = np.diff(mm[16 + 8 * 250:16 + 8 * 250 + 2048 + 1])
+    merged = np.nonzero(n > 1)[0]
+    say("[gpu] many streams: %d of 2048 streams merged" % merged.size)
+    assert 0 < merged.size < 2048
+    rng = np.random.default_rng(151)
+    rows = set((merged[:, None] * 64 + np.arange(64)[None, :]).reshape(-1).tolist())
+    rows |= set(rng.choice(2048 * 64, size=512, replace=False).tolist())
+    check_problem(prob, rows=np.array(sorted(rows)), num_workers=250, what="2048 streams, capped combine grid")
+
+
 def test_many_splits_among_short_streams():
     """One 8192-token stream among fifteen one-tile streams, 128 workers: the
     combine variant that loads 8 splits at once takes its looping path for the
