@@ -430,8 +430,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     const int vis_row = p.causal ? min(max(seqlen - p.s_q + 1 + (rt * kRowTile + qrow) / p.h_q, 0), seqlen) : seqlen;
     // scores of sub-tile u with the tokens this lane's row does not attend set to
     // -inf (this lane: row qrow, tokens 16 tb + 4 h4 + e)
-    auto mask_scores = [&](int u, f32x4& v) {
-      const uint32_t tmask = SPARSE ? sparse_mask(u) : 0u;
+    // (sparse: tmask = sparse_mask(u), read by the caller)
+    auto mask_scores = [&](int u, f32x4& v, uint32_t tmask) {
       const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= vis_min;
       if (!full) {
         asm volatile("");  // a real branch: full sub-tiles skip the masking
@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       if (!redo) {
         // the reference of each row from sub-tile u0 (both token blocks of the row)
         f32x4 v = s;
-        mask_scores(u0, v);
+        mask_scores(u0, v, SPARSE ? sparse_mask(u0) : 0u);
         float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
         mx = row_max16(mx);
         if (h4 == 0) xrow[tb * 64 + qrow] = mx;
@@ -738,6 +738,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         constexpr int kSet = decltype(set_tag)::value;  // FP8: the metadata set this round loads
         const bool issue = kIssue == 1 || u + 3 < u1;  // sub-tile u + 3 exists (workgroup-uniform)
         __builtin_amdgcn_sched_barrier(0);
+        // FP8 sparse: sub-tile u's attended slots, read here so that the
+        // softmax does not wait for the ring read after the score MFMAs
+        // (c4 -4 %; BF16 sparse, which reads its index ring at the softmax
+        // instead, measured 5 % slower this way)
+        const uint32_t tmask_u = SPARSE && FP8 ? sparse_mask(u) : 0u;
         // FP8 dense: the page of sub-tile u + 3, read before this round's K
         // fragments (sparse: its four token rows are read at the load; holding
         // them across the first score MFMAs costs the registers it lacks)
@@ -798,7 +803,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         // softmax of sub-tile u: P = 2^(scale_log2 S - m_ref)
         auto softmax = [&]() __attribute__((always_inline)) {
           f32x4 v = s;
-          mask_scores(u, v);
+          mask_scores(u, v, SPARSE && !FP8 ? sparse_mask(u) : tmask_u);
           const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])) * p.scale_log2;
           m_seen = fmaxf(m_seen, mx);
           overflow |= (m_ref == kNegInf && mx != kNegInf) || mx > m_ref + kRefRoom;
