@@ -6,11 +6,11 @@
 // no tiles (seqlen 0) get o = 0 and lse = -inf.
 //
 // One thread per (query row, 8 columns): it reads the row's split lse values
-// (the same addresses for all 64 threads of a row, so one request per wave),
-// forms L and the weights itself, and issues its split outputs' loads eight
-// at a time, so a workgroup pays one memory round trip per eight splits instead
-// of one per row it visits.  With at most sixteen splits the lse values and
-// the split outputs are loaded together: one round trip in all.
+// (the same addresses for all 64 threads of a row, so one request per wave)
+// together with its split outputs, 8 or 16 splits at a time, and forms L and
+// the weights itself, so a workgroup pays one memory round trip per batch of
+// splits instead of one per row it visits: one in all for up to 8 or 16
+// splits, and an online merge over batches beyond that.
 #include <algorithm>
 
 #include "mla_common.hpp"
@@ -20,7 +20,6 @@ namespace mla {
 namespace {
 
 constexpr int kCombineThreads = 256;  // four rows x 64 threads (8 columns each)
-constexpr int kCombineBatch = 8;  // split outputs in flight per thread
 
 // One thread's 8 columns of one row of the stream.
 template <int kCombineFused>
@@ -91,38 +90,66 @@ __device__ __forceinline__ void combine_row(const DecodeParams& p, int stream, i
     return;
   }
 
-  // more splits: L first (the lse values), then the outputs eight at a time
-  float mx = kNegInf;
-  for (int j = 0; j < n; ++j) mx = fmaxf(mx, lse_col[(int64_t)j * p.R_stream]);
-  float sum = 0.f;
-  if (mx != kNegInf)
-    for (int j = 0; j < n; ++j) sum += __expf(lse_col[(int64_t)j * p.R_stream] - mx);
-  const float L = mx == kNegInf ? kNegInf : mx + __logf(sum);
-  if (L != kNegInf) {
-    for (int j0 = 0; j0 < n; j0 += kCombineBatch) {
-      float4 v[kCombineBatch], v2[kCombineBatch];
-      float w[kCombineBatch];
+  // More splits: one pass over them, kCombineFused at a time (lse values and
+  // outputs loaded together, so one memory round trip per batch), merged
+  // online: m is the largest lse so far, s = sum_j exp(lse_j - m) and
+  // acc = sum_j exp(lse_j - m) o_j, both rescaled when m grows; then
+  // L = m + ln s and o = acc / s.  (Loading the lse values one split after
+  // another in a loop of their own made every split a round trip: a stream of
+  // 32 splits took ~40 us.)
+  float m = kNegInf, s = 0.f;
+  for (int j0 = 0; j0 < n; j0 += kCombineFused) {
+    float lj[kCombineFused];
+    float4 v[kCombineFused], v2[kCombineFused];
 #pragma unroll
-      for (int k = 0; k < kCombineBatch; ++k) {
-        const int j = j0 + k;
-        const float lj = j < n ? lse_col[(int64_t)j * p.R_stream] : kNegInf;
-        // an empty split (lse = -inf) carries weight 0 and its output is not read
-        w[k] = lj == kNegInf ? 0.f : __expf(lj - L);
-        v[k] = w[k] != 0.f ? *(const float4*)(po + j * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
-        v2[k] = w[k] != 0.f ? *(const float4*)(po + j * stride + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int k = 0; k < kCombineBatch; ++k) {
-        acc.x += w[k] * v[k].x;
-        acc.y += w[k] * v[k].y;
-        acc.z += w[k] * v[k].z;
-        acc.w += w[k] * v[k].w;
-        acc2.x += w[k] * v2[k].x;
-        acc2.y += w[k] * v2[k].y;
-        acc2.z += w[k] * v2[k].z;
-        acc2.w += w[k] * v2[k].w;
-      }
+    for (int k = 0; k < kCombineFused; ++k) {
+      const int j = j0 + k;
+      lj[k] = j < n ? lse_col[(int64_t)j * p.R_stream] : kNegInf;
+      v[k] = j < n ? *(const float4*)(po + j * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v2[k] = j < n ? *(const float4*)(po + j * stride + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float bm = kNegInf;
+#pragma unroll
+    for (int k = 0; k < kCombineFused; ++k) bm = fmaxf(bm, lj[k]);
+    if (bm == kNegInf) continue;  // every split of the batch is empty
+    const float nm = fmaxf(m, bm);
+    const float r = m == kNegInf ? 0.f : __expf(m - nm);
+    s *= r;
+    acc.x *= r;
+    acc.y *= r;
+    acc.z *= r;
+    acc.w *= r;
+    acc2.x *= r;
+    acc2.y *= r;
+    acc2.z *= r;
+    acc2.w *= r;
+#pragma unroll
+    for (int k = 0; k < kCombineFused; ++k) {
+      // an empty split (lse = -inf) carries weight 0
+      const float w = lj[k] == kNegInf ? 0.f : __expf(lj[k] - nm);
+      s += w;
+      acc.x += w * v[k].x;
+      acc.y += w * v[k].y;
+      acc.z += w * v[k].z;
+      acc.w += w * v[k].w;
+      acc2.x += w * v2[k].x;
+      acc2.y += w * v2[k].y;
+      acc2.z += w * v2[k].z;
+      acc2.w += w * v2[k].w;
+    }
+    m = nm;
+  }
+  const float L = m == kNegInf ? kNegInf : m + __logf(s);
+  if (m != kNegInf) {
+    const float inv = 1.f / s;
+    acc.x *= inv;
+    acc.y *= inv;
+    acc.z *= inv;
+    acc.w *= inv;
+    acc2.x *= inv;
+    acc2.y *= inv;
+    acc2.z *= inv;
+    acc2.w *= inv;
   }
   write_out(acc, acc2, L);
 }
