@@ -86,9 +86,11 @@ MLA_API int mla_get_metadata_size(int B, int s_q, int h_q, int h_kv, int topk, i
  * num_workers workers (one launch of a single-workgroup kernel on `stream`).
  *   cache_seqlens  device int32 [B], tokens cached per request (>= 0)
  *   is_fp8         1 if the cache will be the 656-byte FP8 layout, else 0 (checked
- *                  to be 0 or 1; the split rule is the same for both caches: on
- *                  every measured workload the finest balanced split, one
- *                  workgroup per compute unit, was fastest, also for FP8)
+ *                  to be 0 or 1).  The split rule is the same for both caches
+ *                  (measured: the cache type did not change the best split):
+ *                  the finest balanced split, one workgroup per compute unit,
+ *                  with splits of at least 4 tiles (256 tokens or index slots)
+ *                  for streams of more than 64 query rows and 2 tiles otherwise
  *   metadata       device buffer of metadata_bytes (>= the size call's value);
  *                  written entirely by the kernel
  * The metadata stays valid for every layer's decode call while cache_seqlens,

@@ -28,12 +28,20 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Smallest number of tiles a worker takes: a split costs a Q reload and a
-// partial-output round trip, so very short splits are not worth it.
-int min_tiles_for(int is_fp8, int topk) {
+// Smallest number of 64-token tiles a worker takes (the per-split cost term).
+// A split costs its workgroups a fixed ~10 us (prologue, epilogue) and writes
+// n_rt x 64 rows of fp32 partials that the combine reads back, so with more
+// row tiles per stream a split must be longer to pay for itself.  Calibrated on
+// decode calls whose total work is under two tiles per worker (with more work
+// the rule does not bind): for 128- and 256-row streams 4 tiles beat 2 by 2-11 %
+// (BF16 dense 27.7 -> 24.4 us, 27.9 -> 25.8, 32.4 -> 30.2; FP8 0-4 %) and 8
+// (for 256 rows) was worse than 4; for 64-row streams 2 beat 4 by 1-11 %
+// (c5-like FP8 sparse 24.1 vs 26.8 us); 1 was worse everywhere.  The cache type
+// and topk did not change the best choice.
+int min_tiles_for(int is_fp8, int topk, int n_rt) {
   (void)is_fp8;
   (void)topk;
-  return 2;
+  return n_rt >= 2 ? 4 : 2;
 }
 
 struct Shape {
@@ -190,8 +198,8 @@ MLA_API int mla_get_metadata(const int32_t* cache_seqlens, int B, int s_q, int h
   sizes(s, W, &meta, &part_o, &ws);
   if (metadata_bytes < meta)
     return fail(MLA_ERR_BUFFER_TOO_SMALL, "metadata needs %zu bytes, got %zu", meta, metadata_bytes);
-  const hipError_t e = mla::launch_sched(cache_seqlens, B, s_q, h_q, topk, W, min_tiles_for(is_fp8, topk), metadata,
-                                         (hipStream_t)stream);
+  const hipError_t e = mla::launch_sched(cache_seqlens, B, s_q, h_q, topk, W, min_tiles_for(is_fp8, topk, s.n_rt),
+                                         metadata, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "scheduler launch");
   return MLA_OK;
 }
@@ -343,7 +351,8 @@ MLA_API int mla_sparse_prefill(const void* q, const void* kv, int64_t s_kv, cons
   int32_t* meta = (int32_t*)(ws + L.meta_off);
   hipError_t e = mla::launch_prefill_setup(seqlen, pages, L.n_pages, (int)s_kv, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill set-up launch");
-  e = mla::launch_sched(seqlen, 1, s_q, h_q, topk, L.W, min_tiles_for(0, topk), meta, (hipStream_t)stream);
+  e = mla::launch_sched(seqlen, 1, s_q, h_q, topk, L.W, min_tiles_for(0, topk, (h_q + mla::kRowTile - 1) / mla::kRowTile),
+                        meta, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "scheduler launch");
   return mla_decode_with_kvcache(q, kv, L.n_pages, pages, L.n_pages, seqlen, 1, s_q, h_q, h_kv, d_qk, d_v,
                                  softmax_scale, meta, L.meta_bytes, L.W, indices, topk, 0, 0, ws + L.ws_off,
