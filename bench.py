@@ -51,8 +51,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 METRIC = "decode TFLOP/s + HBM GB/s vs MI355X roofline; dense bf16 & sparse fp8 MLA"
 HEADLINE = 2
-KERNEL_SOURCES = ["mla_paged_kv_get_amd/csrc/mla_decode.hip", "mla_paged_kv_get_amd/csrc/mla_device.hpp",
-                  "mla_paged_kv_get_amd/csrc/mla_common.hpp"]
+KERNEL_SOURCES = ["mla_paged_kv_get_amd/csrc/mla_decode.hip", "mla_paged_kv_get_amd/csrc/mla_decode_dense.hip",
+                  "mla_paged_kv_get_amd/csrc/mla_device.hpp", "mla_paged_kv_get_amd/csrc/mla_common.hpp"]
 # copy-calibrated FETCH_SIZE + WRITE_SIZE summaries of the decode kernel, per workload
 TRAFFIC_FILES = {
     2: "traffic_mla_decode_kernel_dense_bf16_b64_h128_s4096.json",
@@ -374,7 +374,8 @@ def main():
     h = results[head]
     roofline = dict(h["roofline"])
     roofline.pop("per_launch")
-    roofline.update(kernel="mla_decode_kernel (split-KV decode), mean of per-launch HIP events over the timed steps",
+    kname = "mla_decode_dense_kernel" if head_prob.topk == 0 and not head_prob.is_fp8 else "mla_decode_kernel"
+    roofline.update(kernel=kname + " (split-KV decode), mean of per-launch HIP events over the timed steps",
                     hbm_frac=h["kernel_frac_hbm"], mfma_frac=h["kernel_frac_mfma"])
     line = dict(metric=METRIC, value=h["step_tflops"], unit="TFLOP/s", n_gpus=1, steps=args.steps,
                 warmup=args.warmup, ms_per_step=round(h["step_us"] / 1e3, 5), higher_is_better=True, scaling="weak",

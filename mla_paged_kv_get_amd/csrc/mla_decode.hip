@@ -1,4 +1,6 @@
-// Split-KV decode kernel for MLA over a paged latent cache (gfx950).
+// Split-KV decode kernel for MLA over a paged latent cache (gfx950): the
+// sparse caches and the FP8 cache.  The dense BF16 cache has a kernel of its own
+// with specialised waves (mla_decode_dense.hip).
 //
 // What it computes: for each query row, softmax(scale * q K^T) V over the
 // attended tokens of its stream, where a token's 576-dim latent is K and its
@@ -835,8 +837,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
             if (s2 == 0 && ct == 0) softmax();
             __builtin_amdgcn_sched_barrier(0);
           }
-        // the first K fragments of sub-tile u + 1 (BF16; FP8 spends these VGPRs on
-        // its second tile set and reads them after the barrier)
+        // the first K fragments of sub-tile u + 1 (BF16; FP8 has no registers to
+        // hold them across the barrier and reads them after it)
         if constexpr (kPreK && !kFirst)
           if (kIssue == 1 || u + 1 < u1)
 #pragma unroll
@@ -1024,7 +1026,7 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_decode(const DecodeParams& p, bool is_fp8, hipStream_t stream) {
   const bool sparse = p.topk > 0;
   if (is_fp8) return sparse ? launch_variant<true, true, false>(p, stream) : launch_variant<true, false, false>(p, stream);
-  if (!sparse) return launch_variant<false, false, false>(p, stream);
+  if (!sparse) return launch_decode_dense(p, stream);
   return p.pool_records != 0 ? launch_variant<false, true, true>(p, stream) : launch_variant<false, true, false>(p, stream);
 }
 
