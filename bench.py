@@ -55,8 +55,8 @@ KERNEL_SOURCES = ["mla_paged_kv_get_amd/csrc/mla_decode.hip", "mla_paged_kv_get_
                   "mla_paged_kv_get_amd/csrc/mla_device.hpp", "mla_paged_kv_get_amd/csrc/mla_common.hpp"]
 # copy-calibrated FETCH_SIZE + WRITE_SIZE summaries of the decode kernel, per workload
 TRAFFIC_FILES = {
-    2: "traffic_mla_decode_kernel_dense_bf16_b64_h128_s4096.json",
-    3: "traffic_mla_decode_kernel_dense_bf16_b128_sq2_h128_varlen.json",
+    2: "traffic_mla_decode_dense_kernel_bf16_b64_h128_s4096.json",
+    3: "traffic_mla_decode_dense_kernel_bf16_b128_sq2_h128_varlen.json",
     4: "traffic_mla_decode_kernel_sparse_fp8_b64_h128_topk2048.json",
     5: "traffic_mla_decode_kernel_sparse_fp8_skewed_b8_sq2_h64.json",
 }

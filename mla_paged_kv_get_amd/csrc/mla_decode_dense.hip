@@ -461,44 +461,34 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_dense_kernel(DecodePa
           fetch_page(u0 + kPageAhead);
         }
         if (u0 + 4 < u1) stage_begin(u0 + 4);
-        // end of round u0: sub-tile u0 + 2 has landed
+        // end of round u0: sub-tile u0 + 2 has landed (the score waves read its
+        // first K fragments at the end of round u0 + 1)
         if (issue0)
           barrier_keep<kRoundOps>();
         else
           barrier_keep<0>();
         // ---- rounds --------------------------------------------------------------
-        // round u: the LDS reads that do not depend on this round's loads (P of
-        // sub-tile u - 1, the ring entry of sub-tile u + 4), the loads of sub-tile
-        // u + 3 (their resource from the previous round), the resource of sub-tile
-        // u + 4, then P V of sub-tile u - 1 with V^T of sub-tile u read between the
-        // MFMAs.  A load instruction is accepted at the rate the compute unit's
-        // address path moves 1 KB, so the loads go out first, while the score waves
-        // of the same SIMDs keep the MFMA pipes busy, and the P and ring reads are
-        // in flight meanwhile.  Closing wait: sub-tile u + 2 has landed.
+        // round u: first the loads of sub-tile u + 3 (resource from the previous
+        // round).  The compute unit's address path accepts a load instruction at
+        // the rate it moves 1 KB, so the four PV waves spend about as long issuing
+        // them as the score waves of the same SIMDs spend on their MFMAs.  Then
+        // P V of sub-tile u - 1 with V^T of sub-tile u read between the MFMAs (the
+        // softmax of the score waves runs meanwhile), then the resource of
+        // sub-tile u + 4.  (Issuing the P and ring reads before the loads measured
+        // 10 % slower on the compute-bound s_q = 2 workload.)
         auto round = [&](const int u, MLA_LDS char* __restrict__ kb, MLA_LDS char* __restrict__ nxt)
                          __attribute__((always_inline)) {
           const bool issue = u + 3 < u1;  // workgroup-uniform
-          const bool next = u + 4 < u1;
-          bf16x8 pp[2][2];
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) pp[rb][s2] = pread((u - 1) & 1, rb, s2);
-          int pg = 0;
-          if (next) pg = pg_slot(u + 4)[0];
-          __builtin_amdgcn_sched_barrier(0);
           if (issue) {
 #pragma unroll
             for (int k = 0; k < kLoads; ++k) stage_load(k, nxt);
             fetch_page(u + kPageAhead);
           }
-          __builtin_amdgcn_sched_barrier(0);
-          if (next) {
-            const int page = __builtin_amdgcn_readfirstlane(pg);
-            const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;  // (u + 4) & 1
-            const int valid = __builtin_amdgcn_readfirstlane(min(max(seqlen - (u + 4) * kSub, 0), kSub));
-            st_rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, valid * kBf16TokenBytes, kBufferFlags);
-          }
+          bf16x8 pp[2][2];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) pp[rb][s2] = pread((u - 1) & 1, rb, s2);
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -509,6 +499,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_dense_kernel(DecodePa
               va[s2][ct] = vread(kb, s2, ct);
               __builtin_amdgcn_sched_barrier(0);
             }
+          if (u + 4 < u1) stage_begin(u + 4);
           if (issue)
             barrier_keep<kRoundOps>();  // sub-tile u + 2 has landed
           else
