@@ -52,13 +52,14 @@ PEAK_BF16_TFLOPS = 2500.0
 METRIC = "decode TFLOP/s + HBM GB/s vs MI355X roofline; dense bf16 & sparse fp8 MLA"
 HEADLINE = 2
 KERNEL_SOURCES = ["mla_paged_kv_get_amd/csrc/mla_decode.hip", "mla_paged_kv_get_amd/csrc/mla_decode_dense.hip",
-                  "mla_paged_kv_get_amd/csrc/mla_device.hpp", "mla_paged_kv_get_amd/csrc/mla_common.hpp"]
+                  "mla_paged_kv_get_amd/csrc/mla_decode_fp8.hip", "mla_paged_kv_get_amd/csrc/mla_device.hpp",
+                  "mla_paged_kv_get_amd/csrc/mla_common.hpp"]
 # copy-calibrated FETCH_SIZE + WRITE_SIZE summaries of the decode kernel, per workload
 TRAFFIC_FILES = {
     2: "traffic_mla_decode_dense_kernel_bf16_b64_h128_s4096.json",
     3: "traffic_mla_decode_dense_kernel_bf16_b128_sq2_h128_varlen.json",
-    4: "traffic_mla_decode_kernel_sparse_fp8_b64_h128_topk2048.json",
-    5: "traffic_mla_decode_kernel_sparse_fp8_skewed_b8_sq2_h64.json",
+    4: "traffic_mla_decode_fp8_kernel_sparse_b64_h128_topk2048.json",
+    5: "traffic_mla_decode_fp8_kernel_sparse_skewed_b8_sq2_h64.json",
 }
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
 
@@ -374,7 +375,8 @@ def main():
     h = results[head]
     roofline = dict(h["roofline"])
     roofline.pop("per_launch")
-    kname = "mla_decode_dense_kernel" if head_prob.topk == 0 and not head_prob.is_fp8 else "mla_decode_kernel"
+    kname = ("mla_decode_fp8_kernel" if head_prob.is_fp8 else
+             "mla_decode_dense_kernel" if head_prob.topk == 0 else "mla_decode_kernel")
     roofline.update(kernel=kname + " (split-KV decode), mean of per-launch HIP events over the timed steps",
                     hbm_frac=h["kernel_frac_hbm"], mfma_frac=h["kernel_frac_mfma"])
     line = dict(metric=METRIC, value=h["step_tflops"], unit="TFLOP/s", n_gpus=1, steps=args.steps,

@@ -1025,7 +1025,7 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams& p, bool is_fp8, hipStream_t stream) {
   const bool sparse = p.topk > 0;
-  if (is_fp8) return sparse ? launch_variant<true, true, false>(p, stream) : launch_variant<true, false, false>(p, stream);
+  if (is_fp8) return launch_decode_fp8(p, stream);
   if (!sparse) return launch_decode_dense(p, stream);
   return p.pool_records != 0 ? launch_variant<false, true, true>(p, stream) : launch_variant<false, true, false>(p, stream);
 }
