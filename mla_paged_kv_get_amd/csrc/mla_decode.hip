@@ -1,11 +1,13 @@
-// Split-KV decode kernel for MLA over a paged latent cache (gfx950): the
-// sparse caches and the FP8 cache.  The dense BF16 cache has a kernel of its own
-// with specialised waves (mla_decode_dense.hip).
+// Split-KV decode kernel for MLA over a paged latent cache (gfx950): the sparse
+// BF16 cache (index lists over a BF16 cache, also the sparse prefill).  The dense
+// BF16 cache and the FP8 caches have kernels of their own with specialised waves
+// (mla_decode_dense.hip, mla_decode_fp8.hip).
 //
 // What it computes: for each query row, softmax(scale * q K^T) V over the
-// attended tokens of its stream, where a token's 576-dim latent is K and its
-// first 512 dims are V (FlashMLA source walk-through, data-loading section), and
-// the natural log-sum-exp of the scaled scores.  Each worker processes the KV
+// attended tokens of its stream (slot i of a query token's index list names
+// cache position indices[i], -1 = not attended), where a token's 576-dim latent
+// is K and its first 512 dims are V (FlashMLA source walk-through, data-loading
+// section), and the natural log-sum-exp of the scaled scores.  Each worker processes the KV
 // tile range the scheduler gave it; a stream handled by one worker gets its
 // final o and lse here, otherwise each split leaves a normalised partial o and
 // its lse for the combine kernel (same page, scheduling and combine sections).
@@ -16,12 +18,10 @@
 // fixed per-wave rate, so the second wave doubles the LDS traffic a SIMD can
 // sustain, and each wave's waits (LDS, barrier) are covered by the other's MFMAs.
 // Per 32-token sub-tile of the KV stream:
-//   1. the sub-tile's bf16 rows are staged in a swizzled LDS tile (BF16: direct
-//      global->LDS 16-byte loads, three sub-tiles ahead; FP8: 8-byte code
-//      loads into VGPRs a round before their store, e4m3 -> fp32 (exact) *
-//      scale (RNE) -> bf16 (RNE), then LDS); four buffers hold the sub-tile
-//      being multiplied by V, the next one (whose scores are being computed)
-//      and the two behind it;
+//   1. the sub-tile's bf16 rows are gathered into a swizzled LDS tile by direct
+//      global->LDS 16-byte loads, three sub-tiles ahead; four buffers hold the
+//      sub-tile being multiplied by V, the next one (whose scores are being
+//      computed) and the two behind it;
 //   2. scores: wave w computes S^T for 16 query rows (16 (w & 3) ..) and 16 tokens
 //      (16 (w >> 2) ..) over all 576 dims on v_mfma_f32_16x16x32_bf16, with its Q
 //      rows in VGPRs, so no wave needs another's partial scores;
@@ -35,9 +35,9 @@
 // sub-tile u, then O += P V of sub-tile u - 1 (whose P every wave wrote in the
 // previous round), then the scores of sub-tile u + 1, while sub-tile u + 2
 // streams in; one workgroup barrier per round publishes all of it.
-// Tokens that no row attends (page tails, -1 indices) are loaded as zeros, so
-// every wave issues the same loads per sub-tile and their scores are masked
-// to -inf.
+// Slots that no row attends (-1 indices, slots past the list) are loaded as
+// zeros, so every wave issues the same loads per sub-tile, and their scores are
+// masked to -inf.
 #include "mla_device.hpp"
 
 namespace mla {
@@ -70,9 +70,6 @@ __device__ __forceinline__ void global_load_lds16(const void* src, MLA_LDS void*
 }
 __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t rs, MLA_LDS void* dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
-}
-__device__ __forceinline__ void global_load_lds4(const void* src, MLA_LDS void* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
 // Workgroup barrier after waiting for this wave's LDS operations and for all but
 // its N most recently issued vector memory loads (loads complete in issue order).
@@ -108,7 +105,7 @@ constexpr int kNBuf = 4;
 constexpr int kPOffset = kNBuf * kSubBytes;
 constexpr int kPHalf = 2 * 2 * 64 * 16;
 // Metadata rings (per sub-tile): int32 ring_idx[16][64] (sparse slot indices)
-// and ring_pg[8][64] (their pages; dense: the sub-tile's page).
+// and ring_pg[8][64] (their pages).
 constexpr int kRingIdx = 16;
 constexpr int kRingPg = 8;
 constexpr int kMetaOffset = kPOffset + 2 * kPHalf;
@@ -129,27 +126,14 @@ static_assert(kRowTile * kOutRowF32 <= kNBuf * kSubBytes, "output staging fits t
 // a gather offset past every pool the MUBUF gathers are used for (their
 // resource covers at most kPastPool bytes, and kPastPool + 16 does not wrap)
 constexpr uint32_t kPastPool = 0xFFFFFF00u;
-constexpr int kFp8Loads = 9;  // vector memory operations of one FP8 sub-tile load (4 codes, 4 scales, RoPE)
 static_assert(kSlots == 4 * kDecThreads + kDecThreads / 2, "staging split");
 // Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle.
 constexpr int kBufferFlags = 0x00020000;
 
-// FP8 registers of one sub-tile for this thread: for k = 0..3 the 8 codes of
-// dims 8 lane .. of token 8 k + wave and their scale (scale lane / 16), and 8
-// bytes of RoPE (dims 512 + 4 (lane % 16) ..) of token 8 (lane / 16) + wave.  A
-// wave thus dequantises 64 consecutive 16-byte chunks of one token per store
-// (conflict-free LDS writes) from 512 consecutive code bytes, handles only its
-// own four tokens, and every wave does the same loads and stores.
-struct RawFp8 {
-  u32x2 v[4];
-  float sc[4];
-  u32x2 r;
-};
-
-// BUFG (sparse BF16): token gathers as MUBUF loads against one resource over
-// the whole KV pool (pools below 4 GiB), where a skipped slot's offset lies
-// past the pool and loads zeros; else FLAT loads from per-lane addresses.
-template <bool FP8, bool SPARSE, bool BUFG>
+// BUFG: token gathers as MUBUF loads against one resource over the whole KV pool
+// (pools below 4 GiB), where a skipped slot's offset lies past the pool and
+// loads zeros; else FLAT loads from per-lane addresses.
+template <bool BUFG>
 __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
@@ -198,7 +182,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
   const int bs = ent[0], bt0 = ent[1], es = ent[2], et = ent[3], split0 = ent[4];
   const int32_t* split_off = p.meta + meta_split_offset(p.W);
   const int32_t* first = p.meta + meta_tile_first(p.W, p.n_streams);
-  constexpr int tok_bytes = FP8 ? kFp8TokenBytes : kBf16TokenBytes;
 
   // ---- per-lane constants -------------------------------------------------------
   // K operand of k-step kk (dims 32 kk ..): token 16 tb + l16, chunk 4 kk + h4,
@@ -230,14 +213,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
   // PV step reads: [row block qrow / 32][k-step tb][lane 16 (r4 & 1) + l16 + 32 (h4 / 2)]
   // bf16x8, half h4 & 1.
   const int pw_off = (((r4 >> 1) * 2 + tb) * 64 + 16 * (r4 & 1) + l16 + 32 * (h4 >> 1)) * 16 + 8 * (h4 & 1);
-  // BF16 staging: load k of this thread fills LDS slot s = 512 k + tid, i.e.
-  // token s / 72 of the sub-tile, stored chunk s % 72 (source chunk: that XOR
-  // the token's swizzle); computed when needed, as registers are scarce.
-  auto slot_token = [&](int k) -> int { return min(k * kDecThreads + tid, kSlots - 1) / kTokenChunks; };
-  auto slot_src = [&](int k, int t) -> int {  // source byte offset of load k within token t's row
-    const int s = min(k * kDecThreads + tid, kSlots - 1);
-    return ((s - t * kTokenChunks) ^ tile_swizzle(t)) * 16;
-  };
 
   for (int stream = bs; stream <= es && stream < p.n_streams; ++stream) {
     const int ntiles = first[stream + 1] - first[stream];
@@ -247,22 +222,20 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     const int sid = stream == bs ? split0 : split_off[stream];
     const bool final_out = (split_off[stream + 1] - split_off[stream]) == 1;
 
-    const int b = SPARSE ? stream / p.s_q : stream;
+    const int b = stream / p.s_q;  // a stream is one query token of a request
     const int64_t row_base = (int64_t)stream * p.R_stream;
-    const int seqlen = __builtin_amdgcn_readfirstlane(p.seqlens[b]);  // uniform: keeps what derives from it scalar
     const int32_t* bt_row = p.block_table + (int64_t)b * p.max_blocks;
-    const int32_t* idx_row = SPARSE ? p.indices + (int64_t)stream * p.topk : nullptr;
+    const int32_t* idx_row = p.indices + (int64_t)stream * p.topk;
     // Buffer resources for the direct loads into LDS: MUBUF loads keep the
     // compiler's wait counts exact (a FLAT load into LDS makes it drain every
     // counter at each wait), and an offset past the range loads zeros.
     const __amdgpu_buffer_rsrc_t bt_rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)bt_row, 0, p.max_blocks * 4, kBufferFlags);
     const __amdgpu_buffer_rsrc_t idx_rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)idx_row, 0, SPARSE ? p.topk * 4 : 0, kBufferFlags);
-    // sub-tiles [u0, u1): 32 tokens (dense) or 32 index slots (sparse) each
-    const int limit = SPARSE ? p.topk : seqlen;
+        __builtin_amdgcn_make_buffer_rsrc((void*)idx_row, 0, p.topk * 4, kBufferFlags);
+    // sub-tiles [u0, u1) of 32 index slots
     const int u0 = 2 * lo;
-    const int u1 = min(2 * hi, (limit + kSub - 1) / kSub);
+    const int u1 = min(2 * hi, (p.topk + kSub - 1) / kSub);
 
     // Q fragments (B operand of the score MFMA): row qrow, dims 32 kk + 8 h4 ..
     // The row tile's 64 Q rows (contiguous, 1152 B each) are brought into two
@@ -308,13 +281,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     f32x16 acc[2][2];
 
     // ---- per sub-tile metadata ----------------------------------------------------
-    // Round u issues the tile loads of sub-tile u + 3 (BF16: direct global->LDS
-    // loads, waited for at the end of the next round; FP8: loads into VGPRs,
-    // dequantised into LDS in the next round).  What a round needs to know about a
-    // sub-tile (its cache page, or the index and page of each of its 32 slots) was
-    // fetched earlier by direct loads into LDS rings (16 sub-tiles of indices, 8 of
-    // pages): round u fetches the page of sub-tile u + 6 (dense), or the indices
-    // of sub-tile u + 8 and the pages of sub-tile u + 6's indices (sparse); such a
+    // Round u issues the direct global->LDS loads of sub-tile u + 3, waited for at
+    // the end of the next round.  What a round needs to know about a sub-tile (the
+    // index and page of each of its 32 slots) was fetched earlier by direct loads
+    // into LDS rings (16 sub-tiles of indices, 8 of pages): round u fetches the
+    // indices of sub-tile u + 8 and the pages of sub-tile u + 6's indices; such a
     // load has landed and is visible two rounds later.  No loaded value ever lands
     // in a register it has to carry across rounds: the compiler could only wait
     // for it by draining every load still streaming.
@@ -323,9 +294,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     auto idx_slot = [&](int x) -> MLA_LDS int32_t* { return ring_idx + (x & (kRingIdx - 1)) * 64; };
     auto pg_slot = [&](int x) -> MLA_LDS int32_t* { return ring_pg + (x & (kRingPg - 1)) * 64; };
     // Direct metadata loads into the rings (64 lanes each; lanes 32..63 repeat
-    // 0..31): the indices of sub-tile x, the pages of sub-tile x's indices
-    // (sparse; its indices must be visible), the page of sub-tile x (dense; the
-    // split's last page past its end).
+    // 0..31): the indices of sub-tile x, the pages of sub-tile x's indices (its
+    // indices must be visible).
     auto fetch_idx = [&](int x) {
       const int si = min(x * kSub + l32, p.topk - 1);
       buffer_load_lds4(idx_rs, (MLA_LDS void*)idx_slot(x), (uint32_t)si * 4u);
@@ -335,65 +305,16 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       const bool ok = slot_ok(x) && idx >= 0;
       buffer_load_lds4(bt_rs, (MLA_LDS void*)pg_slot(x), (uint32_t)(ok ? idx >> 6 : 0) * 4u);
     };
-    auto fetch_page = [&](int x) {
-      buffer_load_lds4(bt_rs, (MLA_LDS void*)pg_slot(x), (uint32_t)(min(x, u1 - 1) >> 1) * 4u);
-    };
-    // round u's share: sparse part 0 the indices of sub-tile u + 8, part 1 the
-    // pages of sub-tile u + 6; dense the page of sub-tile u + 6
+    // round u's share: part 0 the indices of sub-tile u + 8, part 1 the pages of
+    // sub-tile u + 6
     auto meta_dma = [&](int u, int part) {
-      if constexpr (SPARSE) {
-        if (part == 0)
-          fetch_idx(u + 8);
-        else
-          fetch_pg(u + 6);
-      } else {
-        fetch_page(u + 6);
-      }
+      if (part == 0)
+        fetch_idx(u + 8);
+      else
+        fetch_pg(u + 6);
     };
-    // FP8 metadata goes through VGPRs instead (its tile loads are VGPR loads,
-    // and the compiler counts register loads exactly):
-    // every wave loads, in round u before that round's tile loads, the indices of
-    // sub-tile u + 8 and the pages of sub-tile u + 6 (dense: its page), and wave 0
-    // writes them into the rings in round u + 1, right after the store that waits
-    // for the tile loads issued before them, so the write costs no extra wait;
-    // they are visible from round u + 2 on, as with the direct loads.
-    struct Fp8Meta {
-      int idx, pg;
-    };
-    auto fp8_meta_load = [&](int u) -> Fp8Meta {
-      int z = 0;
-      asm volatile("" : "+v"(z));  // a per-lane index, so these are vector loads
-      Fp8Meta m;
-      if constexpr (SPARSE) {
-        m.idx = idx_row[min((u + 8) * kSub + l32, p.topk - 1) + z];
-        const int i6 = idx_slot(u + 6)[l32];
-        m.pg = bt_row[(slot_ok(u + 6) && i6 >= 0 ? i6 >> 6 : 0) + z];
-      } else {
-        m.idx = 0;
-        m.pg = bt_row[(min(u + 6, u1 - 1) >> 1) + z];
-      }
-      return m;
-    };
-    // FP8 sparse keeps, in place of each slot's page, the slot's token row
-    // (page * 64 + index % 64, or -1 when the slot is not attended), so a tile load
-    // costs one ring read and a multiply.
-    auto fp8_token_row = [&](int x, int pg) -> int {
-      const int i = idx_slot(x)[l32];
-      return slot_ok(x) && i >= 0 ? pg * kPage + (i & 63) : -1;
-    };
-    auto fp8_meta_publish = [&](int u, const Fp8Meta& m) {  // round u's loads, by wave 0
-      if (wave_s == 0) {
-        if constexpr (SPARSE) {
-          idx_slot(u + 8)[lane] = m.idx;
-          pg_slot(u + 6)[lane] = fp8_token_row(u + 6, m.pg);
-        } else {
-          pg_slot(u + 6)[lane] = m.pg;
-        }
-      }
-    };
-    // prologue: the ring entries of sub-tiles u0 .. u0 + 5 (pages) and, sparse,
-    // u0 .. u0 + 7 (indices), one sub-tile per wave; ends with a barrier after
-    // which they are visible
+    // prologue: the ring entries of sub-tiles u0 .. u0 + 5 (pages) and u0 .. u0 + 7
+    // (indices); ends with a barrier after which they are visible
     // (Q's loads start here too: waves 0..3 issue them and only pass the
     // barriers, while waves 4..7 fetch the entries, two sub-tiles each, and
     // wait for them.)
@@ -401,66 +322,43 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       if (wave_s < 4) {
         stage_q(0, buffer(u0 + 2));
         stage_q(1, buffer(u0 + 3));
-        if constexpr (SPARSE) lds_barrier();
+        lds_barrier();
         lds_barrier();
       } else {
         const int x = wave_s - 4;
-        if constexpr (SPARSE) {
-          fetch_idx(u0 + x);
-          fetch_idx(u0 + x + 4);
-          tile_barrier_drain();
-          fetch_pg(u0 + x);
-          if (x < 2) fetch_pg(u0 + x + 4);
-        } else {
-          fetch_page(u0 + x);
-          if (x < 2) fetch_page(u0 + x + 4);
-        }
+        fetch_idx(u0 + x);
+        fetch_idx(u0 + x + 4);
+        tile_barrier_drain();
+        fetch_pg(u0 + x);
+        if (x < 2) fetch_pg(u0 + x + 4);
         tile_barrier_drain();
       }
     };
-    // attended mask of sub-tile u's 32 slots (sparse)
-    auto sparse_mask = [&](int u) -> uint32_t {
-      const bool ok = FP8 ? pg_slot(u)[l32] >= 0 : slot_ok(u) && idx_slot(u)[l32] >= 0;
-      return (uint32_t)__ballot(ok);
-    };
-    // Dense visibility: the tokens [0, vis) a row attends.  Non-causal: the whole
-    // sequence.  Causal: the s_q query tokens are the last s_q positions, so the
-    // row of query token i = row / h_q sees [0, seqlen - s_q + 1 + i) (usage
-    // example of the geoz.com.cn page: causal=True).  vis_min is the smallest
-    // window of the stream (query token 0).
-    const int vis_min = p.causal ? max(seqlen - p.s_q + 1, 0) : seqlen;
-    const int vis_row = p.causal ? min(max(seqlen - p.s_q + 1 + (rt * kRowTile + qrow) / p.h_q, 0), seqlen) : seqlen;
-    // scores of sub-tile u with the tokens this lane's row does not attend set to
-    // -inf (this lane: row qrow, tokens 16 tb + 4 h4 + e)
-    // (sparse: tmask = sparse_mask(u), read by the caller)
+    // attended mask of sub-tile u's 32 slots
+    auto sparse_mask = [&](int u) -> uint32_t { return (uint32_t)__ballot(slot_ok(u) && idx_slot(u)[l32] >= 0); };
+    // scores of sub-tile u with the slots this lane's row does not attend set to
+    // -inf (this lane: row qrow, slots 16 tb + 4 h4 + e; tmask = sparse_mask(u),
+    // read by the caller)
     auto mask_scores = [&](int u, f32x4& v, uint32_t tmask) {
-      const bool full = SPARSE ? tmask == 0xFFFFFFFFu : (u + 1) * kSub <= vis_min;
-      if (!full) {
+      if (tmask != 0xFFFFFFFFu) {
         asm volatile("");  // a real branch: full sub-tiles skip the masking
         // tok0 is made opaque so that the compiler does not keep 4 token numbers
         // live across the loop
         int tok0 = 16 * tb + 4 * h4;
         asm volatile("" : "+v"(tok0));
-        const int vcount = vis_row - u * kSub - tok0;
         const uint32_t lmask = tmask >> tok0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = SPARSE ? ((lmask >> e) & 1u) != 0 : e < vcount;
-          v[e] = ok ? v[e] : kNegInf;
-        }
+        for (int e = 0; e < 4; ++e) v[e] = ((lmask >> e) & 1u) != 0 ? v[e] : kNegInf;
       }
     };
     // ---- staging ------------------------------------------------------------------
-    // BF16 direct loads of sub-tile u: this thread's five (or four) 16-byte
-    // pieces.  Dense tiles use buffer loads against a resource that covers only
-    // the sub-tile's tokens inside the sequence, so the pieces of tokens past
-    // its end load zeros; sparse tiles load from per-lane global addresses (the
-    // zero token when a slot is not attended).  stage_begin reads the
-    // sub-tile's ring entry; stage_load issues piece k.
-    __amdgpu_buffer_rsrc_t st_rs;  // dense: the sub-tile's bytes inside the sequence
-    int st_tk[kLoads];             // sparse: token row (or -1) of each of this thread's pieces
+    // Direct loads of sub-tile u: this thread's five (or four) 16-byte pieces,
+    // gathered from per-slot token rows (the zero token, or an offset past the
+    // pool, when a slot is not attended).  stage_begin reads the sub-tile's ring
+    // entries; stage_load issues piece k.
+    int st_tk[kLoads];  // token row (or -1) of each of this thread's pieces
     auto stage_begin = [&](int u) {
-      if constexpr (SPARSE) {
+      {
         const int idx = idx_slot(u)[l32];
         const int pg = pg_slot(u)[l32];
         const int tok = (slot_ok(u) && idx >= 0) ? pg * kPage + (idx & 63) : -1;
@@ -471,17 +369,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         asm volatile("" : "+v"(to));
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) st_tk[k] = __shfl(tok, min(k * kDecThreads + to, kSlots - 1) / kTokenChunks);
-      } else {
-        const int page = __builtin_amdgcn_readfirstlane(pg_slot(u)[0]);
-        const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
-        // tokens inside the sequence (scalar: the resource must be uniform)
-        const int valid = __builtin_amdgcn_readfirstlane(min(max(seqlen - u * kSub, 0), kSub));
-        st_rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, valid * kBf16TokenBytes, kBufferFlags);
       }
     };
     auto stage_load = [&](int k, MLA_LDS char* buf) {  // k < kLoads - 1, or waves 0..3
       MLA_LDS void* dst = (MLA_LDS void*)(buf + k * (kDecThreads * 16) + wave_s * 1024);
-      if constexpr (SPARSE) {
+      {
         // the piece's token and source offset, recomputed from an opaque copy of
         // tid rather than kept live across the loop
         int to = tid;
@@ -500,9 +392,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
           const uint8_t* src = (tk >= 0 ? p.kv + (int64_t)tk * kBf16TokenBytes : g_zero_token) + chunk;
           global_load_lds16((const void*)src, dst);
         }
-      } else {
-        const int t = slot_token(k);
-        buffer_load_lds16(st_rs, dst, (uint32_t)(t * kBf16TokenBytes + slot_src(k, t)));
       }
     };
     auto stage_bf16 = [&](int u, MLA_LDS char* buf) {
@@ -510,72 +399,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
 #pragma unroll
       for (int k = 0; k < kLoads - 1; ++k) stage_load(k, buf);
       if (wave_s < 4) stage_load(kLoads - 1, buf);
-    };
-    // The four tokens 8 k + wave are the same for the whole wave, so their ring
-    // entries go to scalars and their addresses are scalar arithmetic; a token
-    // that is not attended (or lies past the sequence or the split) reads the
-    // zero token.
-    // The ring entries a tile load of sub-tile u needs (sparse: its four token
-    // rows; dense: its page).  Waiting for an LDS read also waits for every
-    // older one, so a dense round reads its page before its K fragments.
-    struct Fp8Rows {
-      int v[4];
-    };
-    auto fp8_rows = [&](int u) -> Fp8Rows {
-      Fp8Rows t;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) t.v[k] = SPARSE ? pg_slot(u)[8 * k + wave_s] : (k == 0 ? pg_slot(u)[0] : 0);
-      return t;
-    };
-    auto load_fp8 = [&](int u, RawFp8& r, const Fp8Rows& rows) {
-      int lo = lane;
-      asm volatile("" : "+v"(lo));  // per-lane offsets recomputed here, not kept live
-      const uint8_t* pt[4];
-      if constexpr (SPARSE) {
-        int tk[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          tk[k] = __builtin_amdgcn_readfirstlane(rows.v[k]);
-          pt[k] = u < u1 && tk[k] >= 0 ? p.kv + (int64_t)tk[k] * tok_bytes : g_zero_token;
-        }
-      } else {
-        // past the split the ring slot may never have been written: its page is not used
-        const int valid = u < u1 ? seqlen - u * kSub : 0;  // tokens of the sub-tile in the sequence
-        const int page = __builtin_amdgcn_readfirstlane(rows.v[0]);
-        const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * tok_bytes;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int t = 8 * k + wave_s;
-          pt[k] = t < valid ? base + t * tok_bytes : g_zero_token;
-        }
-      }
-      // unsigned lane offsets: the loads take the scalar token address plus a
-      // 32-bit per-lane offset
-      const uint32_t ul = (uint32_t)lo;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        r.v[k] = *(const u32x2*)(pt[k] + 8u * ul);
-        r.sc[k] = *(const float*)(pt[k] + (uint32_t)kFp8Dims + 4u * (ul >> 4));
-      }
-      // RoPE bytes: lanes 16 k .. 16 k + 15 cover token 8 k + wave
-      const uint32_t kr = ul >> 4;
-      const uint8_t* prr = kr == 0 ? pt[0] : kr == 1 ? pt[1] : kr == 2 ? pt[2] : pt[3];
-      r.r = *(const u32x2*)(prr + (uint32_t)(kFp8Dims + 16) + 8u * (ul & 15u));
-    };
-    // Token 8 k + wave's swizzle is 4 bit1(wave) + 2 (k & 1), so the store
-    // address of chunk `lane` is one of two per-lane bases plus 8 k token rows.
-    auto store_fp8 = [&](const RawFp8& r, MLA_LDS char* buf) {
-      int lo = lane;
-      asm volatile("" : "+v"(lo));  // recomputed here rather than kept live across the loop
-      const int b0 = (wave_s * kTokenChunks + (lo ^ (4 * ((wave_s >> 1) & 1)))) * 16;
-      const int b1 = (wave_s * kTokenChunks + (lo ^ (4 * ((wave_s >> 1) & 1) + 2))) * 16;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x2 a = dequant4(r.v[k].x, r.sc[k]), b = dequant4(r.v[k].y, r.sc[k]);
-        *(MLA_LDS u32x4*)(buf + ((k & 1) ? b1 : b0) + 8 * k * kBf16TokenBytes) = u32x4{a.x, a.y, b.x, b.y};
-      }
-      const int tr = 8 * (lo >> 4) + wave_s;
-      *(MLA_LDS u32x2*)(buf + tile_slot(tr, 64 + ((lo & 15) >> 1)) * 16 + 8 * (lo & 1)) = r.r;
     };
     // ---- operand reads ------------------------------------------------------------
     auto kread = [&](MLA_LDS char* kb, int kk) -> bf16x8 {
@@ -610,66 +433,35 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
     float m_ref = kNegInf, m_seen = kNegInf, l_sum = 0.f;
     bool redo = false;
     int pass = 0;  // at most two: the second pass runs with the split's row maximum
-    // K fragments read ahead of their score MFMA.  FP8 holds one sub-tile in
-    // VGPRs between its load and its store (loaded one round ahead): a second
-    // set (two rounds ahead) left registers for only two or three fragments
-    // ahead, and the reads' LDS latency then cost more than the lead gained
-    // (c4 -4..-6 us with one set and four fragments).
+    // K fragments read ahead of their score MFMA (the first ones before the
+    // round's barrier)
     constexpr int kAhead = 4;
-    constexpr bool kPreK = !FP8;           // the first ones read before the round's barrier
-    constexpr int kPRead = FP8 ? 16 : 13;  // score MFMA after which the P fragments are read
+    constexpr int kPRead = 13;  // score MFMA after which the P fragments are read
     do {
       l_sum = 0.f;
       bool overflow = false;
 
       // ---- prologue ---------------------------------------------------------------
       // Q goes through the buffers of sub-tiles u0 + 2 and u0 + 3 before they
-      // hold tiles.  BF16: sub-tiles u0 and u0 + 1 and Q issued; u0 and Q landed;
-      // Q read; then u0 + 2 issued into its buffer.  FP8: u0 and u0 + 1 loaded and
-      // stored, Q landed and read, u0 + 2 in flight in VGPRs.  Then S
-      // of u0 and the reference, whose barrier ends every wave's reads of Q
-      // before round u0 stores sub-tile u0 + 2 there.
-      RawFp8 raw[2];       // FP8: a sub-tile in VGPRs between its load and its store (raw[1]: prologue only)
-      Fp8Meta fmeta[2];    // FP8: metadata loaded in a round, written the next (alternating sets)
-      if constexpr (FP8) {
-        meta_fill();
-        if constexpr (SPARSE) {
-          // the prologue's pages become token rows
-          if (wave_s < 6) {
-            const int x = u0 + wave_s;
-            const int tk = fp8_token_row(x, pg_slot(x)[l32]);
-            pg_slot(x)[lane] = tk;
-          }
-          lds_barrier();
-        }
-        load_fp8(u0, raw[0], fp8_rows(u0));
-        load_fp8(u0 + 1, raw[1], fp8_rows(u0 + 1));
-        store_fp8(raw[0], buffer(u0));
-        store_fp8(raw[1], buffer(u0 + 1));
-        load_fp8(u0 + 2, raw[0], fp8_rows(u0 + 2));
-        // Q's direct loads (waves 0..3, issued before the metadata fill) are
-        // older than the 9 register loads just issued
-        barrier_keep_seen<kFp8Loads>();
-        read_q(buffer(u0 + 2), buffer(u0 + 3));
-      } else {
-        meta_fill();
-        // Sub-tile u0 + 1 is loaded even when the split ends first (the dense
-        // resource and the sparse zero token keep such loads in bounds; the
-        // buffer is not read), so every path issues the same loads.
-        stage_bf16(u0, buffer(u0));
-        stage_bf16(u0 + 1, buffer(u0 + 1));
-        // u0 and Q (waves 0..3, older) landed; u0 + 1 (5 or 4 loads per wave)
-        // stays in flight
-        if (wave_s < 4)
-          barrier_keep<kLoads>();
-        else
-          barrier_keep<kLoads - 1>();
-        read_q(buffer(u0 + 2), buffer(u0 + 3));
-        lds_barrier();  // every wave has read Q before sub-tile u0 + 2 lands there
-        // (loaded whether or not it exists, as u0 + 1; waited for with u0 + 1 at
-        // the first round's closing wait)
-        stage_bf16(u0 + 2, buffer(u0 + 2));
-      }
+      // hold tiles: sub-tiles u0 and u0 + 1 and Q issued; u0 and Q landed; Q read;
+      // then u0 + 2 issued into its buffer.  Then S of u0 and the reference.
+      meta_fill();
+      // Sub-tile u0 + 1 is loaded even when the split ends first (the zero
+      // token keeps such loads in bounds; the buffer is not read), so every path
+      // issues the same loads.
+      stage_bf16(u0, buffer(u0));
+      stage_bf16(u0 + 1, buffer(u0 + 1));
+      // u0 and Q (waves 0..3, older) landed; u0 + 1 (5 or 4 loads per wave)
+      // stays in flight
+      if (wave_s < 4)
+        barrier_keep<kLoads>();
+      else
+        barrier_keep<kLoads - 1>();
+      read_q(buffer(u0 + 2), buffer(u0 + 3));
+      lds_barrier();  // every wave has read Q before sub-tile u0 + 2 lands there
+      // (loaded whether or not it exists, as u0 + 1; waited for with u0 + 1 at
+      // the first round's closing wait)
+      stage_bf16(u0 + 2, buffer(u0 + 2));
       // K fragments kk .. kk + kAhead - 1 of the next score step (rolling)
       bf16x8 kf[kAhead];
       f32x4 s;  // S^T of the sub-tile whose softmax comes next
@@ -687,7 +479,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       if (!redo) {
         // the reference of each row from sub-tile u0 (both token blocks of the row)
         f32x4 v = s;
-        mask_scores(u0, v, SPARSE ? sparse_mask(u0) : 0u);
+        mask_scores(u0, v, sparse_mask(u0));
         float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
         mx = row_max16(mx);
         if (h4 == 0) xrow[tb * 64 + qrow] = mx;
@@ -695,10 +487,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         const float m0 = fmaxf(xrow[qrow], xrow[64 + qrow]) * p.scale_log2;
         m_ref = m0 == kNegInf ? kNegInf : m0 + kRefLift;
         // xrow is next written after the loop, behind at least one round's barrier
-      } else if constexpr (FP8) {
-        // (the reference's barrier is what otherwise separates the reads of Q
-        // from round u0's store into the same buffer)
-        lds_barrier();
       }
 
       // (zeroed here, after the prologue's loads, not before them)
@@ -714,9 +502,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       // One round u, entered after the barrier that ended round u - 1, with S(u)
       // in s (round u0: from the prologue), the first K fragments of sub-tile u in
       // kf, V^T of sub-tile u - 1 in va and P of sub-tile u - 1 in LDS:
-      //   scores of sub-tile u (round u0: computed already), with the staging of a
-      //   later sub-tile (BF16: direct loads of u + 3; FP8: store of u + 2, then
-      //   its registers reloaded with u + 3) between the MFMAs;
+      //   scores of sub-tile u (round u0: computed already), with the direct loads
+      //   of sub-tile u + 3 between the MFMAs;
       //   O += P V of sub-tile u - 1, with the softmax of sub-tile u, its P write
       //   and the V^T reads of sub-tile u between the MFMAs;
       //   the first K fragments of sub-tile u + 1; one barrier.
@@ -729,54 +516,26 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
       // BF16 load accounting: a round that stages issues exactly kLoads vector
       // memory operations per wave (waves 0..3 five tile pieces, waves 4..7 four
       // and one metadata load), so its closing wait is one count for every wave.
-      auto round = [&](auto first_tag, auto issue_tag, auto set_tag, auto kself_tag, const int u,
+      auto round = [&](auto first_tag, auto issue_tag, auto kself_tag, const int u,
                        MLA_LDS char* __restrict__ kb, MLA_LDS char* __restrict__ kn,
                        MLA_LDS char* __restrict__ nxt) __attribute__((always_inline)) {
         constexpr bool kFirst = decltype(first_tag)::value != 0;
-        // this round reads its first K fragments itself (FP8 always; BF16 in the
-        // round after u0, whose sub-tile was still landing when round u0 ended)
+        // this round reads its first K fragments itself (the round after u0,
+        // whose sub-tile was still landing when round u0 ended)
         constexpr bool kSelfK = decltype(kself_tag)::value != 0;
         constexpr int kIssue = decltype(issue_tag)::value;
-        constexpr int kSet = decltype(set_tag)::value;  // FP8: the metadata set this round loads
         const bool issue = kIssue == 1 || u + 3 < u1;  // sub-tile u + 3 exists (workgroup-uniform)
         __builtin_amdgcn_sched_barrier(0);
-        // FP8 sparse: sub-tile u's attended slots, read here so that the
-        // softmax does not wait for the ring read after the score MFMAs
-        // (c4 -4 %; BF16 sparse, which reads its index ring at the softmax
-        // instead, measured 5 % slower this way)
-        const uint32_t tmask_u = SPARSE && FP8 ? sparse_mask(u) : 0u;
-        // FP8 dense: the page of sub-tile u + 3, read before this round's K
-        // fragments (sparse: its four token rows are read at the load; holding
-        // them across the first score MFMAs costs the registers it lacks)
-        Fp8Rows nrows;
-        if constexpr (FP8 && !SPARSE) nrows = fp8_rows(u + 3);
         // staging work placed after score MFMA kk
         auto stage_step = [&](int kk) __attribute__((always_inline)) {
-          if constexpr (FP8) {
-            // The loads into VGPRs are issued whether or not their sub-tile exists
-            // (past the split they read in-bounds bytes that are never used), so
-            // that the compiler's wait for them is a count on every path.
-            if (kk == 1) {
-              store_fp8(raw[0], nxt);  // sub-tile u + 2, loaded in the previous round
-              if (!kFirst) fp8_meta_publish(u - 1, fmeta[kSet ^ 1]);
-            }
-            if (kk == 2) fmeta[kSet] = fp8_meta_load(u);
-            if (kk == 3) {
-              if constexpr (SPARSE)
-                load_fp8(u + 3, raw[0], fp8_rows(u + 3));
-              else
-                load_fp8(u + 3, raw[0], nrows);
-            }
-          } else {
-            if (issue) {
-              if (kk == 0) stage_begin(u + 3);
-              if (kk % 3 == 1 && kk / 3 < kLoads - 1) stage_load(kk / 3, nxt);
-              if (kk == 3 * (kLoads - 1) + 1) {
-                if (wave_s < 4)
-                  stage_load(kLoads - 1, nxt);
-                else  // dense: waves 4..7 load the same page; sparse: 4, 5 part 0, 6, 7 part 1
-                  meta_dma(u, (wave_s >> 1) & 1);
-              }
+          if (issue) {
+            if (kk == 0) stage_begin(u + 3);
+            if (kk % 3 == 1 && kk / 3 < kLoads - 1) stage_load(kk / 3, nxt);
+            if (kk == 3 * (kLoads - 1) + 1) {
+              if (wave_s < 4)
+                stage_load(kLoads - 1, nxt);
+              else  // waves 4, 5: metadata part 0; 6, 7: part 1
+                meta_dma(u, (wave_s >> 1) & 1);
             }
           }
         };
@@ -805,7 +564,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
         // softmax of sub-tile u: P = 2^(scale_log2 S - m_ref)
         auto softmax = [&]() __attribute__((always_inline)) {
           f32x4 v = s;
-          mask_scores(u, v, SPARSE && !FP8 ? sparse_mask(u) : tmask_u);
+          mask_scores(u, v, sparse_mask(u));
           const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])) * p.scale_log2;
           m_seen = fmaxf(m_seen, mx);
           overflow |= (m_ref == kNegInf && mx != kNegInf) || mx > m_ref + kRefRoom;
@@ -837,42 +596,29 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
             if (s2 == 0 && ct == 0) softmax();
             __builtin_amdgcn_sched_barrier(0);
           }
-        // the first K fragments of sub-tile u + 1 (BF16; FP8 has no registers to
-        // hold them across the barrier and reads them after it)
-        if constexpr (kPreK && !kFirst)
+        // the first K fragments of sub-tile u + 1
+        if constexpr (!kFirst)
           if (kIssue == 1 || u + 1 < u1)
 #pragma unroll
             for (int kk = 0; kk < kAhead; ++kk) kf[kk] = kread(kn, kk);
-        if constexpr (FP8) {
-          lds_barrier();  // sub-tile u + 2 went through registers
-        } else if (issue) {
+        if (issue) {
           barrier_keep<kLoads>();  // the previous round's loads (sub-tile u + 2, metadata) have landed
         } else {
           tile_barrier_drain();
         }
       };
-      constexpr int kStageAhead = FP8 ? 2 : 3;  // the sub-tile a round stages
-      round(Tag<1>{}, Tag<-1>{}, Tag<0>{}, Tag<0>{}, u0, buffer(u0), buffer(u0 + 1), buffer(u0 + kStageAhead));
+      constexpr int kStageAhead = 3;  // the sub-tile a round stages
+      round(Tag<1>{}, Tag<-1>{}, Tag<0>{}, u0, buffer(u0), buffer(u0 + 1), buffer(u0 + kStageAhead));
       int u = u0 + 1;
-      if constexpr (FP8) {
-        // unrolled by two: the metadata sets alternate between rounds
-        for (; u + 1 < u1; u += 2) {
-          round(Tag<0>{}, Tag<-1>{}, Tag<1>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
-          round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, Tag<1>{}, u + 1, buffer(u + 1), buffer(u + 2),
-                buffer(u + 1 + kStageAhead));
-        }
-        if (u < u1) round(Tag<0>{}, Tag<-1>{}, Tag<1>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
-      } else {
-        if (u < u1) {
-          round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
-          ++u;
-        }
-        // main loop: every round stages an existing sub-tile; then the last rounds
-        for (; u + 3 < u1; ++u)
-          round(Tag<0>{}, Tag<1>{}, Tag<0>{}, Tag<0>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
-        for (; u < u1; ++u)
-          round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, Tag<0>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+      if (u < u1) {
+        round(Tag<0>{}, Tag<-1>{}, Tag<1>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+        ++u;
       }
+      // main loop: every round stages an existing sub-tile; then the last rounds
+      for (; u + 3 < u1; ++u)
+        round(Tag<0>{}, Tag<1>{}, Tag<0>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
+      for (; u < u1; ++u)
+        round(Tag<0>{}, Tag<-1>{}, Tag<0>{}, u, buffer(u), buffer(u + 1), buffer(u + kStageAhead));
 
       // PV of the last sub-tile
       {
@@ -1008,10 +754,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
   }
 }
 
-template <bool FP8, bool SPARSE, bool BUFG>
+template <bool BUFG>
 hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
   static bool attr_set = false;
-  auto kern = mla_decode_kernel<FP8, SPARSE, BUFG>;
+  auto kern = mla_decode_kernel<BUFG>;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
@@ -1027,7 +773,7 @@ hipError_t launch_decode(const DecodeParams& p, bool is_fp8, hipStream_t stream)
   const bool sparse = p.topk > 0;
   if (is_fp8) return launch_decode_fp8(p, stream);
   if (!sparse) return launch_decode_dense(p, stream);
-  return p.pool_records != 0 ? launch_variant<false, true, true>(p, stream) : launch_variant<false, true, false>(p, stream);
+  return p.pool_records != 0 ? launch_variant<true>(p, stream) : launch_variant<false>(p, stream);
 }
 
 }  // namespace mla
