@@ -371,13 +371,15 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_dense_kernel(DecodePa
       const int x = cv;
       // direct loads of a sub-tile: a resource over the sub-tile's tokens inside
       // the sequence (pieces past its end load zeros), from its ring entry
+      // (pgv: the sub-tile's ring entry, read by the caller)
       __amdgpu_buffer_rsrc_t st_rs;
-      auto stage_begin = [&](int u) {
-        const int page = __builtin_amdgcn_readfirstlane(pg_slot(u)[0]);
+      auto stage_begin_pg = [&](int u, int pgv) {
+        const int page = __builtin_amdgcn_readfirstlane(pgv);
         const uint8_t* base = p.kv + ((int64_t)page * kPage + (u & 1) * kSub) * kBf16TokenBytes;
         const int valid = __builtin_amdgcn_readfirstlane(min(max(seqlen - u * kSub, 0), kSub));
         st_rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, valid * kBf16TokenBytes, kBufferFlags);
       };
+      auto stage_begin = [&](int u) { stage_begin_pg(u, pg_slot(u)[0]); };
       // source offset of this thread's piece k within the sub-tile: slot
       // 256 k + (tid - 256) holds token slot / 72, stored chunk slot % 72 (the
       // source chunk is that XOR the token's swizzle)
@@ -474,8 +476,9 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_dense_kernel(DecodePa
         // them as the score waves of the same SIMDs spend on their MFMAs.  Then
         // P V of sub-tile u - 1 with V^T of sub-tile u read between the MFMAs (the
         // softmax of the score waves runs meanwhile), then the resource of
-        // sub-tile u + 4.  (Issuing the P and ring reads before the loads measured
-        // 10 % slower on the compute-bound s_q = 2 workload.)
+        // sub-tile u + 4, whose ring entry is read before the MFMAs (after them it
+        // cost 3 % on the compute-bound s_q = 2 workload).  (Issuing the P and ring
+        // reads before the loads measured 10 % slower there.)
         auto round = [&](const int u, MLA_LDS char* __restrict__ kb, MLA_LDS char* __restrict__ nxt)
                          __attribute__((always_inline)) {
           const bool issue = u + 3 < u1;  // workgroup-uniform
@@ -489,6 +492,9 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_dense_kernel(DecodePa
           for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) pp[rb][s2] = pread((u - 1) & 1, rb, s2);
+          // the ring entry of sub-tile u + 4 (landed two rounds ago), read here so
+          // that its latency passes under the MFMAs rather than before the barrier
+          const int pg4 = pg_slot(u + 4)[0];
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -499,7 +505,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_dense_kernel(DecodePa
               va[s2][ct] = vread(kb, s2, ct);
               __builtin_amdgcn_sched_barrier(0);
             }
-          if (u + 4 < u1) stage_begin(u + 4);
+          if (u + 4 < u1) stage_begin_pg(u + 4, pg4);
           if (issue)
             barrier_keep<kRoundOps>();  // sub-tile u + 2 has landed
           else

@@ -86,7 +86,13 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t rs, MLA_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
 }
 
-// A token of zeros: the source for tokens no query row attends.
+// Offset past the pool for tokens no query row attends (pool-wide buffer loads
+// read zeros there): the pool is at most this many bytes, and this plus a
+// token's 656 bytes does not wrap.
+constexpr uint32_t kPastPoolF8 = 0xFFFFF000u;
+
+// A token of zeros: the source for tokens no query row attends when the pool
+// is too large for 32-bit offsets (then each token's address is a pointer).
 __device__ __attribute__((aligned(64))) uint8_t g_zero_fp8_token[kFp8TokenBytes] = {0};
 
 // FP8 registers of one wave's share of a sub-tile: for k = 0..3 the 8 codes of
@@ -106,7 +112,7 @@ struct Fp8Meta {
   int idx, pg;
 };
 
-template <bool SPARSE>
+template <bool SPARSE, bool BUFG>
 __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
@@ -235,6 +241,44 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
     auto load_fp8 = [&](int u, RawFp8& r, const Fp8Rows& rows) {
       int lo2 = lane;
       asm volatile("" : "+v"(lo2));  // per-lane offsets recomputed here, not kept live
+      if constexpr (BUFG) {
+        // One resource over the pool: a token's byte offset, or past the pool.
+        // (A select between a token's pointer and the zero token made the
+        // compiler reload the zero token's address by a scalar load in the
+        // loop, and the wait for that load drained the wave's LDS operations,
+        // twice per round: c4 -4 % without it.)
+        const __amdgpu_buffer_rsrc_t pool_rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, 0, p.pool_records, kBufferFlags);
+        uint32_t toff[4];
+        if constexpr (SPARSE) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int tk = __builtin_amdgcn_readfirstlane(rows.v[k]);
+            toff[k] = u < u1 && tk >= 0 ? (uint32_t)tk * (uint32_t)kFp8TokenBytes : kPastPoolF8;
+          }
+        } else {
+          const int valid = u < u1 ? seqlen - u * kSub : 0;
+          const int page = __builtin_amdgcn_readfirstlane(rows.v[0]);
+          const uint32_t base = (uint32_t)(page * kPage + (u & 1) * kSub) * (uint32_t)kFp8TokenBytes;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int t = 8 * k + wave_s;
+            toff[k] = t < valid ? base + (uint32_t)t * (uint32_t)kFp8TokenBytes : kPastPoolF8;
+          }
+        }
+        const uint32_t ul = (uint32_t)lo2;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          r.v[k] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(pool_rs, toff[k] + 8u * ul, 0, 0));
+          r.sc[k] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(pool_rs, toff[k] + (uint32_t)kFp8Dims + 4u * (ul >> 4), 0, 0));
+        }
+        const uint32_t kr = ul >> 4;
+        const uint32_t tr = kr == 0 ? toff[0] : kr == 1 ? toff[1] : kr == 2 ? toff[2] : toff[3];
+        r.r = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(pool_rs, tr + (uint32_t)(kFp8Dims + 16) + 8u * (ul & 15u), 0, 0));
+        return;
+      }
       const uint8_t* pt[4];
       if constexpr (SPARSE) {
 #pragma unroll
@@ -480,8 +524,9 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
         // then the softmax and the first K fragments of sub-tile u + 1.
         for (int u = u0 + 1; u < u1; ++u) {
           // the ring reads of the round first: a wait for an LDS read also waits
-          // for the stores issued before it
-          const uint32_t tmask = SPARSE ? sparse_mask(u) : 0u;
+          // for the stores issued before it (the sparse mask's entry is tested
+          // after the scores, so that its wait does not hold the first MFMAs)
+          int tmv = SPARSE ? pg_slot(u)[l32] : 0;
           const Fp8Rows rows3 = fp8_rows(u + 3);
           const int i6 = SPARSE ? idx_slot(u + 6)[l32] : 0;
           MLA_LDS char* nxt = buffer(u + 2);
@@ -493,6 +538,8 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
             if (kk == 2) fm = fp8_meta_load(u, i6);
             if (kk == 3) load_fp8(u + 3, raw, rows3);
           });
+          asm volatile("" : "+v"(tmv));
+          const uint32_t tmask = SPARSE ? (uint32_t)__ballot(tmv >= 0) : 0u;
           softmax(u, tmask);
           if (u + 1 < u1)
 #pragma unroll
@@ -734,10 +781,10 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
   }
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool BUFG>
 hipError_t launch_fp8(const DecodeParams& p, hipStream_t stream) {
   static bool attr_set = false;
-  auto kern = mla_decode_fp8_kernel<SPARSE>;
+  auto kern = mla_decode_fp8_kernel<SPARSE, BUFG>;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
@@ -750,7 +797,10 @@ hipError_t launch_fp8(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_fp8(const DecodeParams& p, hipStream_t stream) {
-  return p.topk > 0 ? launch_fp8<true>(p, stream) : launch_fp8<false>(p, stream);
+  // pool-wide buffer loads while every token offset and the past-pool offset fit 32 bits
+  const bool bufg = p.pool_records != 0 && p.pool_records <= kPastPoolF8;
+  if (p.topk > 0) return bufg ? launch_fp8<true, true>(p, stream) : launch_fp8<true, false>(p, stream);
+  return bufg ? launch_fp8<false, true>(p, stream) : launch_fp8<false, false>(p, stream);
 }
 
 }  // namespace mla

@@ -413,3 +413,30 @@ def test_sparse_bf16_pool_past_4gib():
     o, lse = flat(o, lse)
     o_ref, lse_ref = oracle.problem_decode(prob)
     compare(o, lse, o_ref, lse_ref, prob.name)
+
+
+@pytest.mark.parametrize("topk", [0, 192])
+def test_fp8_pool_past_4gib(topk):
+    """FP8 token loads from pools whose byte offsets fit 32 bits go through one
+    buffer resource over the pool (unattended tokens read past its end); larger
+    pools take per-token addresses and a zero token.  The same problem's pages at
+    the top of a 4.3 GB FP8 pool must give the oracle's result too (dense and
+    sparse)."""
+    kind = "sparse" if topk else "dense"
+    prob = mi.make_problem("%s fp8 in a 4.3 GB pool" % kind, 2, 1, 64, [900, 300], seed=112 + topk, topk=topk,
+                           is_fp8=True, n_invalid=11 if topk else 0)
+    d = to_device(prob)
+    n = prob.num_blocks
+    page_bytes = d["kvcache"][0].numel() * d["kvcache"].element_size()
+    big_pages = (int(4.3e9) // page_bytes) + n
+    big = torch.empty((big_pages,) + tuple(d["kvcache"].shape[1:]), dtype=d["kvcache"].dtype, device=DEV)
+    big[big_pages - n:] = d["kvcache"]
+    d["kvcache"] = big
+    d["block_table"] = d["block_table"] + (big_pages - n)
+    say("[gpu] %s (%d pages, %.2f GB)" % (prob.name, big_pages, big_pages * page_bytes / 1e9))
+    o, lse, _ = run_gpu(prob, num_workers=5, dev_inputs=d)
+    del big, d
+    torch.cuda.empty_cache()
+    o, lse = flat(o, lse)
+    o_ref, lse_ref = oracle.problem_decode(prob)
+    compare(o, lse, o_ref, lse_ref, prob.name)
