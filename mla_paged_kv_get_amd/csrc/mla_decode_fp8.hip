@@ -22,7 +22,12 @@
 // Every wave decodes 4 tokens of each sub-tile (tokens 8 k + w): their codes,
 // scales and RoPE bytes go into VGPRs one round before the wave writes them as
 // bf16 into the swizzled LDS tile, so the dequantising VALU work is spread over
-// all 8 waves (staging by the PV waves alone made them the bottleneck: c4 +15 %).
+// all 8 waves (staging by the PV waves alone made them the bottleneck: c4 +15 %;
+// three of the score wave's four tokens, or two, and the rest by the PV waves:
+// +8 % and +13 %).  A wave issues about one VALU instruction every 7 clocks
+// (two waves of a SIMD at that rate each), so each wave's VALU count per round
+// is kept down: per-lane offsets stay in registers, the metadata is the PV
+// waves' work, and the sparse mask is computed once for both row blocks.
 // Round u (one barrier): the score waves compute S and P of sub-tile u, the PV
 // waves P V of sub-tile u - 1 and V^T of sub-tile u, and every wave writes its
 // share of sub-tile u + 2 (loaded in round u - 1) and loads its share of
@@ -108,9 +113,6 @@ struct RawFp8 {
 struct Fp8Rows {
   int v[4];
 };
-struct Fp8Meta {
-  int idx, pg;
-};
 
 template <bool SPARSE, bool BUFG>
 __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodeParams p) {
@@ -182,10 +184,12 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
     // ---- metadata ---------------------------------------------------------------
     // What a sub-tile's loads need (its page, or each slot's token row) sits in
     // LDS rings written ahead: the prologue fills them by direct loads; then
-    // round u loads into VGPRs the indices of sub-tile u + 8 and the pages of
-    // sub-tile u + 6 (sparse; dense: the page of sub-tile u + 6), and wave 0 writes
-    // them into the rings in round u + 1, after the store that waits for the loads
-    // issued after them (a wait for a register load waits for every older load).
+    // round u loads into VGPRs the indices of sub-tile u + 8 (sparse, wave 4) and
+    // the pages of sub-tile u + 6 (wave 5; sparse: of its slots' indices), and the
+    // same waves write them into the rings in round u + 1, after the store that
+    // waits for the loads issued after them (a wait for a register load waits for
+    // every older load).  They are PV waves: a wave issues about one VALU
+    // instruction every 7 clocks, and the score waves carry more per round.
     // Sparse rings then hold each slot's token row (page * 64 + index % 64, or -1
     // when the slot is not attended).
     auto slot_ok = [&](int u) { return u < u1 && u * kSub + l32 < p.topk; };  // sparse slot l32 exists
@@ -203,33 +207,21 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
     auto fetch_page = [&](int x) {
       buffer_load_lds4(bt_rs, (MLA_LDS void*)pg_slot(x), (uint32_t)(min(x, u1 - 1) >> 1) * 4u);
     };
-    // (i6: the ring's index of slot l32 of sub-tile u + 6, read by the caller)
-    auto fp8_meta_load = [&](int u, int i6) -> Fp8Meta {
+    auto meta_idx_load = [&](int u) -> int {  // sparse: the indices of sub-tile u + 8
       int z = 0;
-      asm volatile("" : "+v"(z));  // a per-lane index, so these are vector loads
-      Fp8Meta m;
-      if constexpr (SPARSE) {
-        m.idx = idx_row[min((u + 8) * kSub + l32, p.topk - 1) + z];
-        m.pg = bt_row[(slot_ok(u + 6) && i6 >= 0 ? i6 >> 6 : 0) + z];
-      } else {
-        m.idx = 0;
-        m.pg = bt_row[(min(u + 6, u1 - 1) >> 1) + z];
-      }
-      return m;
+      asm volatile("" : "+v"(z));  // a per-lane index, so this is a vector load
+      return idx_row[min((u + 8) * kSub + l32, p.topk - 1) + z];
+    };
+    // (i6: the ring's index of slot l32 of sub-tile u + 6, read by the caller)
+    auto meta_pg_load = [&](int u, int i6) -> int {  // the pages of sub-tile u + 6
+      int z = 0;
+      asm volatile("" : "+v"(z));
+      if constexpr (SPARSE) return bt_row[(slot_ok(u + 6) && i6 >= 0 ? i6 >> 6 : 0) + z];
+      return bt_row[(min(u + 6, u1 - 1) >> 1) + z];
     };
     auto fp8_token_row = [&](int x, int pg) -> int {
       const int i = idx_slot(x)[l32];
       return slot_ok(x) && i >= 0 ? pg * kPage + (i & 63) : -1;
-    };
-    auto fp8_meta_publish = [&](int u, const Fp8Meta& m) {  // round u's loads, by wave 0
-      if (wave_s == 0) {
-        if constexpr (SPARSE) {
-          idx_slot(u + 8)[lane] = m.idx;
-          pg_slot(u + 6)[lane] = fp8_token_row(u + 6, m.pg);
-        } else {
-          pg_slot(u + 6)[lane] = m.pg;
-        }
-      }
     };
     // ---- FP8 staging (every wave: tokens 8 k + wave) -------------------------------
     auto fp8_rows = [&](int u) -> Fp8Rows {
@@ -239,8 +231,11 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
       return t;
     };
     auto load_fp8 = [&](int u, RawFp8& r, const Fp8Rows& rows) {
+      // per-lane offsets: kept live across the loop where registers allow (pool
+      // offsets: recomputing them cost the score wave ~27 VALU instructions a
+      // round, c4 -6 %), else recomputed from an opaque copy of the lane
       int lo2 = lane;
-      asm volatile("" : "+v"(lo2));  // per-lane offsets recomputed here, not kept live
+      if constexpr (!BUFG) asm volatile("" : "+v"(lo2));
       if constexpr (BUFG) {
         // One resource over the pool: a token's byte offset, or past the pool.
         // (A select between a token's pointer and the zero token made the
@@ -314,7 +309,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
     // address of chunk `lane` is one of two per-lane bases plus 8 k token rows.
     auto store_fp8 = [&](const RawFp8& r, MLA_LDS char* buf) {
       int lo2 = lane;
-      asm volatile("" : "+v"(lo2));  // recomputed here rather than kept live across the loop
+      if constexpr (!BUFG) asm volatile("" : "+v"(lo2));
       const int b0 = (wave_s * kTokenChunks + (lo2 ^ (4 * ((wave_s >> 1) & 1)))) * 16;
       const int b1 = (wave_s * kTokenChunks + (lo2 ^ (4 * ((wave_s >> 1) & 1) + 2))) * 16;
 #pragma unroll
@@ -466,10 +461,32 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
           }
         };
         auto softmax = [&](int u, uint32_t tmask) __attribute__((always_inline)) {
+          f32x4 vm[2] = {s[0], s[1]};
+          if (SPARSE ? tmask != 0xFFFFFFFFu : (u + 1) * kSub > vis_min) {
+            asm volatile("");  // a real branch: full sub-tiles skip the masking
+            int tok0 = 16 * tb + 4 * h4;
+            asm volatile("" : "+v"(tok0));
+            if constexpr (SPARSE) {
+              // the slots are the same for both row blocks
+              const uint32_t lmask = tmask >> tok0;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const bool ok = ((lmask >> e) & 1u) != 0;
+                vm[0][e] = ok ? vm[0][e] : kNegInf;
+                vm[1][e] = ok ? vm[1][e] : kNegInf;
+              }
+            } else {
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb) {
+                const int vcount = vis_row[rb] - u * kSub - tok0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vm[rb][e] = e < vcount ? vm[rb][e] : kNegInf;
+              }
+            }
+          }
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
-            f32x4 v = s[rb];
-            mask_scores(u, rb, v, tmask);
+            const f32x4 v = vm[rb];
             const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
             m_seen[rb] = fmaxf(m_seen[rb], mx);
             overflow |= mx > thr[rb];
@@ -507,10 +524,9 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
           }
         }
         set_ref();
-        // round u0: sub-tile u0 + 2 into Q's first buffer, the metadata of round u0,
-        // sub-tile u0 + 3 into the registers
+        // round u0: sub-tile u0 + 2 into Q's first buffer, sub-tile u0 + 3 into the
+        // registers
         store_fp8(raw, buffer(u0 + 2));
-        Fp8Meta fm = fp8_meta_load(u0, SPARSE ? idx_slot(u0 + 6)[l32] : 0);
         load_fp8(u0 + 3, raw, fp8_rows(u0 + 3));
         softmax(u0, tmask0);
         if (u0 + 1 < u1)
@@ -519,8 +535,7 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
         lds_barrier();  // end of round u0: sub-tile u0 + 2 is in LDS
         // ---- rounds ------------------------------------------------------------------
         // round u: S of sub-tile u; after its first MFMAs this wave's share of
-        // sub-tile u + 2 goes to LDS, wave 0 publishes the metadata of round u - 1,
-        // and the metadata of round u and the share of sub-tile u + 3 are loaded;
+        // sub-tile u + 2 goes to LDS and the share of sub-tile u + 3 is loaded;
         // then the softmax and the first K fragments of sub-tile u + 1.
         for (int u = u0 + 1; u < u1; ++u) {
           // the ring reads of the round first: a wait for an LDS read also waits
@@ -528,14 +543,9 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
           // after the scores, so that its wait does not hold the first MFMAs)
           int tmv = SPARSE ? pg_slot(u)[l32] : 0;
           const Fp8Rows rows3 = fp8_rows(u + 3);
-          const int i6 = SPARSE ? idx_slot(u + 6)[l32] : 0;
           MLA_LDS char* nxt = buffer(u + 2);
           scores(buffer(u), false, [&](int kk) __attribute__((always_inline)) {
-            if (kk == 1) {
-              store_fp8(raw, nxt);
-              fp8_meta_publish(u - 1, fm);
-            }
-            if (kk == 2) fm = fp8_meta_load(u, i6);
+            if (kk == 1) store_fp8(raw, nxt);
             if (kk == 3) load_fp8(u + 3, raw, rows3);
           });
           asm volatile("" : "+v"(tmv));
@@ -651,6 +661,10 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
         // round u0: sub-tile u0 + 2 into Q's first buffer, sub-tile u0 + 3 into the
         // registers
         store_fp8(raw, buffer(u0 + 2));
+        // the metadata loads and ring writes are waves 4 and 5's
+        int fmi = 0, fmp = 0;
+        if (SPARSE && wave_s == 4) fmi = meta_idx_load(u0);
+        if (wave_s == 5) fmp = meta_pg_load(u0, SPARSE ? idx_slot(u0 + 6)[l32] : 0);
         load_fp8(u0 + 3, raw, fp8_rows(u0 + 3));
         lds_barrier();  // end of round u0
         // ---- rounds ------------------------------------------------------------------
@@ -662,12 +676,23 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
           // the ring entries of sub-tile u + 3 first: a wait for an LDS read also
           // waits for the stores issued before it
           const Fp8Rows rows3 = fp8_rows(u + 3);
+          const int i6 = SPARSE ? idx_slot(u + 6)[l32] : 0;
           bf16x8 pp[2][2];
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) pp[rb][s2] = pread((u - 1) & 1, rb, s2);
           store_fp8(raw, nxt);
+          // round u - 1's metadata into the rings, round u's loaded (sparse: the
+          // indices by wave 4, the token rows by wave 5)
+          if (SPARSE && wave_s == 4) {
+            idx_slot(u + 7)[lane] = fmi;
+            fmi = meta_idx_load(u);
+          }
+          if (wave_s == 5) {
+            pg_slot(u + 5)[lane] = SPARSE ? fp8_token_row(u + 5, fmp) : fmp;
+            fmp = meta_pg_load(u, i6);
+          }
           load_fp8(u + 3, raw, rows3);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
