@@ -24,7 +24,8 @@ constexpr int kThreads = 256;  // 4 waves
 // Metadata: int32 words.
 //   [0, 16)                         header (MH_* below)
 //   [16, 16 + 8 W)                  per-worker schedule: begin_stream, begin_tile,
-//                                   end_stream, end_tile (end exclusive), first_split
+//                                   end_stream, end_tile (end exclusive), first_split,
+//                                   the first piece's end tile, its stream's splits
 //   [.., + n_streams + 1)           split_offset: first split id of each stream
 //   [.., + n_streams + 1)           tile_first: first global tile of each stream
 constexpr int kMetaHeader = 16;

@@ -155,16 +155,27 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
   }
   const int32_t* ent = p.meta + kMetaHeader + (int64_t)w * kSchedStride;
   const int bs = ent[0], bt0 = ent[1], es = ent[2], et = ent[3], split0 = ent[4];
+  const int hi0 = ent[5], nsplit0 = ent[6];  // the first piece's end tile and its stream's splits
   const int32_t* split_off = p.meta + meta_split_offset(p.W);
   const int32_t* first = p.meta + meta_tile_first(p.W, p.n_streams);
 
   for (int stream = bs; stream <= es && stream < p.n_streams; ++stream) {
-    const int ntiles = first[stream + 1] - first[stream];
-    const int lo = stream == bs ? bt0 : 0;
-    const int hi = stream == es ? et : ntiles;
+    // The first piece comes from the schedule entry alone, so its Q, metadata
+    // and tile loads wait for one metadata round trip; later pieces read their
+    // stream's tile count and splits.
+    int lo = 0, hi, sid, nsplit;
+    if (stream == bs) {
+      lo = bt0;
+      hi = hi0;
+      sid = split0;
+      nsplit = nsplit0;
+    } else {
+      hi = stream == es ? et : first[stream + 1] - first[stream];
+      sid = split_off[stream];
+      nsplit = split_off[stream + 1] - sid;
+    }
     if (hi <= lo) continue;
-    const int sid = stream == bs ? split0 : split_off[stream];
-    const bool final_out = (split_off[stream + 1] - split_off[stream]) == 1;
+    const bool final_out = nsplit == 1;
 
     const int b = SPARSE ? stream / p.s_q : stream;
     const int64_t row_base = (int64_t)stream * p.R_stream;

@@ -137,6 +137,10 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t*
       v[2] = es;
       v[3] = es < n ? (int32_t)(whi - first[es]) : 0;
       v[4] = (int32_t)(split_off[bs] + (w - (int64_t)first[bs] / q));
+      // the first piece's end tile and its stream's split count, so that the
+      // decode kernel starts its first piece from this entry alone
+      v[5] = es == bs ? v[3] : first[bs + 1] - first[bs];
+      v[6] = split_off[bs + 1] - split_off[bs];
     }
     for (int k = 0; k < kSchedStride; ++k) e[k] = v[k];
   }

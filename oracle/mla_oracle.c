@@ -304,6 +304,11 @@ void oracle_mla_decode(const uint16_t* q, int B, int s_q, int h_q, const uint8_t
  * Output (int32):
  *   sched[w * 8 + 0..4] = begin_stream, begin_tile, end_stream, end_tile,
  *                         first_split  (end exclusive; begin == end when idle)
+ *   sched[w * 8 + 5, 6] = the end tile of the worker's first piece (in its first
+ *                         stream) and that stream's number of splits: derived
+ *                         from the words above and split_offset, stored so that
+ *                         a worker learns its first piece from one read (0 when
+ *                         idle)
  *   split_offset[i]     = first split id of stream i, i = 0..n_streams
  *                         (split_offset[n_streams] = total splits)
  * Returns the number of streams.
@@ -351,6 +356,8 @@ int oracle_schedule(const int32_t* cache_seqlens, int B, int s_q, int topk, int 
     e[2] = es;
     e[3] = es < n_streams ? (int32_t)(hi - first[es]) : 0;
     e[4] = (int32_t)(split_offset[bs] + (w - first[bs] / q));
+    e[5] = es == bs ? e[3] : (int32_t)tiles[bs];
+    e[6] = split_offset[bs + 1] - split_offset[bs];
   }
   free(tiles);
   free(first);
