@@ -420,12 +420,15 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
         if constexpr (SPARSE) lds_barrier();
         lds_barrier();
         rows_from_pages();
-        RawFp8 raw, raw1;
+        // sub-tiles u0 .. u0 + 2 loaded at once (a third register set is free
+        // before Q and the accumulators are), u0 and u0 + 1 stored
+        RawFp8 raw, raw1, raw2;
         load_fp8(u0, raw, fp8_rows(u0));
         load_fp8(u0 + 1, raw1, fp8_rows(u0 + 1));
+        load_fp8(u0 + 2, raw2, fp8_rows(u0 + 2));
         store_fp8(raw, buffer(u0));
         store_fp8(raw1, buffer(u0 + 1));
-        load_fp8(u0 + 2, raw, fp8_rows(u0 + 2));
+        raw = raw2;
         // Q's direct loads are older than the 9 register loads just issued
         barrier_keep_seen<kFp8Loads>();
         bf16x8 qf[2][18];
@@ -651,12 +654,15 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
           tile_barrier_drain();
         }
         rows_from_pages();
-        RawFp8 raw, raw1;
+        // sub-tiles u0 .. u0 + 2 loaded at once (a third register set is free
+        // before Q and the accumulators are), u0 and u0 + 1 stored
+        RawFp8 raw, raw1, raw2;
         load_fp8(u0, raw, fp8_rows(u0));
         load_fp8(u0 + 1, raw1, fp8_rows(u0 + 1));
+        load_fp8(u0 + 2, raw2, fp8_rows(u0 + 2));
         store_fp8(raw, buffer(u0));
         store_fp8(raw1, buffer(u0 + 1));
-        load_fp8(u0 + 2, raw, fp8_rows(u0 + 2));
+        raw = raw2;
         barrier_keep_seen<kFp8Loads>();  // sub-tiles u0 and u0 + 1 are in LDS
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
