@@ -123,7 +123,10 @@ MLA_API int mla_get_metadata(const int32_t* cache_seqlens, int B, int s_q, int h
  *                  lse = -inf).  The usage example of "FlashMLA: DeepSeek's
  *                  efficient MLA decoding kernel" passes causal=True for
  *                  autoregressive decoding.
- *   workspace      device buffer of workspace_bytes (>= the size call's value)
+ *   workspace      device buffer of workspace_bytes (>= the size call's value);
+ *                  no initial contents needed.  A split row that attends no
+ *                  token writes only its lse (-inf), not its partial output,
+ *                  and the combine gives it weight 0
  *   o              device bf16 [B, s_q, h_q, 512] (output)
  *   lse            device fp32 [B, s_q, h_q] (output, natural log)
  * Preconditions not checked on the device: indices in {-1} U [0, seqlen_b);
@@ -154,7 +157,7 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
  * on one GPU shares that GPU's array, so calls that overlap in time on one GPU
  * (concurrent streams, several host threads) race and give wrong results;
  * calls ordered on one stream are safe.  Nothing in the array needs clearing
- * between calls: each call writes every workspace entry it reads.
+ * between calls: each call writes every workspace value it uses.
  */
 #define MLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 MLA_API int mla_decode_with_kvcache_noalloc(const void* q, const void* kvcache, int64_t num_blocks,

@@ -125,8 +125,10 @@ __device__ __forceinline__ void combine_row(const DecodeParams& p, int stream, i
     acc2.w *= r;
 #pragma unroll
     for (int k = 0; k < kCombineFused; ++k) {
-      // an empty split (lse = -inf) carries weight 0
-      const float w = lj[k] == kNegInf ? 0.f : __expf(lj[k] - nm);
+      // an empty split (lse = -inf) carries weight 0; its output was not
+      // written and is not used
+      if (lj[k] == kNegInf) continue;
+      const float w = __expf(lj[k] - nm);
       s += w;
       acc.x += w * v[k].x;
       acc.y += w * v[k].y;
@@ -230,7 +232,8 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_wide_kernel(Decod
     acc2.w *= r;
 #pragma unroll
     for (int k = 0; k < kWideBatch; ++k) {
-      const float w = lj[k] == kNegInf ? 0.f : __expf(lj[k] - nm);
+      if (lj[k] == kNegInf) continue;  // an empty split: output not written
+      const float w = __expf(lj[k] - nm);
       s += w;
       acc.x += w * v[k].x;
       acc.y += w * v[k].y;

@@ -751,12 +751,17 @@ __global__ __launch_bounds__(kDecThreads, 1) void mla_decode_kernel(DecodeParams
           if (row < nrows) *(u32x4*)(dst + row * (kDV * 2) + off) = *(MLA_LDS u32x4*)(smem + row * kOutRowBf16 + off);
         }
       } else {
+        // a row that attends nothing in this split (lse = -inf) leaves its
+        // partial output unwritten: the combine gives such a split weight 0
+        // and does not use its output
+        const float lrow = xrow[to & 63] + xrow[64 + (to & 63)];
+        const uint64_t live = __ballot(lrow > 0.f);
         char* dst = (char*)(p.part_o + ((int64_t)sid * p.R_stream + rt * kRowTile) * kDV);
 #pragma unroll
         for (int k = 0; k < kRowTile * kDV * 4 / 16 / kDecThreads; ++k) {
           const int c = k * kDecThreads + to;
           const int row = c >> 7, off = (c & 127) * 16;
-          if (row < nrows) *(u32x4*)(dst + row * (kDV * 4) + off) = *(MLA_LDS u32x4*)(smem + row * kOutRowF32 + off);
+          if (row < nrows && ((live >> row) & 1u)) *(u32x4*)(dst + row * (kDV * 4) + off) = *(MLA_LDS u32x4*)(smem + row * kOutRowF32 + off);
         }
       }
     }

@@ -218,6 +218,47 @@ def test_empty_streams_and_all_masked():
     check_problem(sp, num_workers=3)
 
 
+EMPTY_SPLITS = [
+    # index lists padded with -1 past short requests: whole splits attend nothing
+    # (16 or 32 splits per stream: the combine's batched and per-row paths)
+    dict(name="sparse bf16 padded lists", B=2, s_q=1, h_q=64, seqlens=[5000, 700], topk=4096, recipe="clip",
+         seed=131),
+    dict(name="sparse fp8 padded lists", B=2, s_q=2, h_q=64, seqlens=[3000, 500], topk=2048, recipe="clip",
+         is_fp8=True, seed=132),
+    dict(name="sparse fp8 h128 padded lists", B=3, s_q=1, h_q=128, seqlens=[2100, 90, 1000], topk=2048,
+         recipe="clip", is_fp8=True, seed=133),
+    # 65 causal query tokens x 2 heads (3 row tiles, so splits of 4 tiles): query
+    # token i sees positions <= seqlen - 65 + i, so the first ~20 see nothing of
+    # the split that starts at position 256 and the others do
+    dict(name="dense bf16 causal 130 rows", B=2, s_q=65, h_q=2, seqlens=[300, 290], seed=134, causal=True),
+    dict(name="dense fp8 causal 130 rows", B=2, s_q=65, h_q=2, seqlens=[300, 270], seed=135, is_fp8=True,
+         causal=True),
+]
+
+
+@pytest.mark.parametrize("case", EMPTY_SPLITS, ids=[c["name"] for c in EMPTY_SPLITS])
+@pytest.mark.parametrize("W", [16, 64, 256])
+def test_empty_split_rows_with_nan_workspace(case, W):
+    """A split row that attends no token writes only its lse (-inf); its partial
+    output stays as the workspace held it (here NaN bytes), and the combine must
+    give it weight 0 without touching the result."""
+    import mla_paged_kv_get_amd as mla
+
+    c = dict(case)
+    causal = c.pop("causal", False)
+    prob = mi.make_problem(c.pop("name"), **c)
+    say("[gpu] %s (W=%d, NaN workspace)" % (prob.name, W))
+    d = to_device(prob)
+    meta = mla.mla_get_metadata(d["cache_seqlens"], prob.s_q, prob.h_q, 1, prob.topk, prob.is_fp8, W)
+    ws = torch.full((meta.workspace_bytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    o, lse = mla.mla_decode_with_kvcache(d["q"], d["kvcache"], d["block_table"], d["cache_seqlens"], 512, meta,
+                                         d["indices"], prob.is_fp8, prob.softmax_scale, workspace=ws, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = flat(o, lse)
+    o_ref, lse_ref = oracle.problem_decode(prob, None, causal)
+    compare(o, lse, o_ref, lse_ref, "%s W=%d" % (prob.name, W))
+
+
 @pytest.mark.parametrize("is_fp8", [False, True])
 def test_single_token(is_fp8):
     prob = mi.make_problem("single token", 1, 1, 64, [300], seed=41, topk=64, is_fp8=is_fp8)
