@@ -95,7 +95,11 @@ MLA_API int mla_get_metadata_size(int B, int s_q, int h_q, int h_kv, int topk, i
  *                  written entirely by the kernel
  * The metadata stays valid for every layer's decode call while cache_seqlens,
  * B, s_q, h_q, topk, is_fp8 and num_workers are unchanged; reusing it after a
- * length change gives wrong results (not detected).
+ * length change gives wrong results (not detected).  It also holds one arrival
+ * counter per (stream, 64-row tile), zeroed here, that merging decode calls
+ * (mla_set_merge_mode) use and leave at zero: merging decode calls that share
+ * one metadata buffer must therefore not run at the same time (issue them on
+ * one stream, as the layers of a step are).
  */
 MLA_API int mla_get_metadata(const int32_t* cache_seqlens, int B, int s_q, int h_q, int h_kv, int topk, int is_fp8,
                              int num_workers, int32_t* metadata, size_t metadata_bytes, void* stream);
@@ -197,6 +201,32 @@ MLA_API int mla_sparse_prefill(const void* q, const void* kv, int64_t s_kv, cons
 
 /* Thread-local, NUL-terminated description of this thread's last failed call ("" if none). */
 MLA_API const char* mla_last_error(void);
+
+/*
+ * Where a decode call merges the partial results of split streams (FlashMLA
+ * source walk-through, combine section: split results are folded by their lse
+ * in a combine step, whose launch gap the pages' kernels hide by overlapping
+ * the two kernels).  Modes, for the calling thread's later decode calls:
+ *   MLA_MERGE_OFF  (default) the combine kernel, launched after the decode
+ *                  kernel on the same stream
+ *   MLA_MERGE_ON   the decode kernel merges, where the host can prove that no
+ *                  stream has more than 4 splits (sparse: from topk and the
+ *                  worker count; dense: from max_blocks; otherwise the combine
+ *                  kernel runs): each split writes its partial output through to
+ *                  memory and counts itself in on the metadata's arrival counter
+ *                  of its 64-row tile; the last split of the tile to arrive
+ *                  merges the stream's splits and writes o and lse, and no
+ *                  combine kernel is launched.  On MI355X this measured slower
+ *                  than the combine kernel on every shape tried (small calls
+ *                  included: its device-coherent writes, the count and the
+ *                  merge's reads are serial memory round trips), so it is an
+ *                  option, not the default.
+ * Results are bit-identical in both modes.  Returns MLA_ERR_INVALID_ARG for any
+ * other value.
+ */
+#define MLA_MERGE_OFF 0
+#define MLA_MERGE_ON 1
+MLA_API int mla_set_merge_mode(int mode);
 
 /*
  * Bench hook: timing of the split-KV decode kernel alone.  While set on the

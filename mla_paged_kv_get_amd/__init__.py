@@ -7,10 +7,11 @@ thin ctypes binding with the same function names.  mla_sparse_prefill runs
 the sparse path over one contiguous KV sequence (many query tokens, each with
 its own index list).
 """
-from .binding import (DecodeKernelTimer, Metadata, MlaError, mla_debug_dequant_fp8, mla_decode_with_kvcache,
-                      mla_decode_with_kvcache_noalloc, mla_get_metadata,
-                      mla_get_metadata_size, mla_last_error, mla_sparse_prefill, lib, LIB_PATH)
+from .binding import (DecodeKernelTimer, Metadata, MlaError, MLA_MERGE_OFF, MLA_MERGE_ON,
+                      mla_debug_dequant_fp8, mla_decode_with_kvcache, mla_decode_with_kvcache_noalloc,
+                      mla_get_metadata, mla_get_metadata_size, mla_last_error, mla_set_merge_mode,
+                      mla_sparse_prefill, lib, LIB_PATH)
 
-__all__ = ["DecodeKernelTimer", "Metadata", "MlaError", "mla_debug_dequant_fp8", "mla_decode_with_kvcache",
-           "mla_decode_with_kvcache_noalloc", "mla_get_metadata",
-           "mla_get_metadata_size", "mla_last_error", "mla_sparse_prefill", "lib", "LIB_PATH"]
+__all__ = ["DecodeKernelTimer", "Metadata", "MlaError", "MLA_MERGE_OFF", "MLA_MERGE_ON",
+           "mla_debug_dequant_fp8", "mla_decode_with_kvcache", "mla_decode_with_kvcache_noalloc", "mla_get_metadata",
+           "mla_get_metadata_size", "mla_last_error", "mla_set_merge_mode", "mla_sparse_prefill", "lib", "LIB_PATH"]

@@ -66,8 +66,21 @@ def lib() -> ctypes.CDLL:
         L.mla_debug_dequant_fp8.argtypes = [P, I64, P, P]
         L.mla_set_decode_kernel_events.restype = I
         L.mla_set_decode_kernel_events.argtypes = [P, P]
+        L.mla_set_merge_mode.restype = I
+        L.mla_set_merge_mode.argtypes = [I]
         _lib = L
     return _lib
+
+
+MLA_MERGE_OFF, MLA_MERGE_ON = 0, 1
+
+
+def mla_set_merge_mode(mode: int) -> None:
+    """Where this thread's later decode calls merge split results: MLA_MERGE_OFF
+    (default: the combine kernel) or MLA_MERGE_ON (in the decode kernel, by the
+    last split of each row tile, when every stream provably has at most 4
+    splits)."""
+    _check(lib().mla_set_merge_mode(int(mode)), "mla_set_merge_mode")
 
 
 def mla_last_error() -> str:

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/mla_decode.h"
@@ -15,6 +16,8 @@ namespace {
 thread_local char g_err[512] = "";
 // bench hook: events recorded around the decode kernel (both set or both null)
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+// when the decode kernel merges the splits itself (mla_set_merge_mode)
+thread_local int g_merge_mode = MLA_MERGE_OFF;
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -47,6 +50,27 @@ int min_tiles_for(int is_fp8, int topk, int n_rt) {
 struct Shape {
   int n_streams, R, RT, n_rt;
 };
+
+// Whether a decode call merges its splits in the decode kernel (the last split
+// of each row tile merges; no combine launch).  That needs every stream to have
+// at most kMergeMaxSplits splits, which the host proves from what it knows:
+// sparse streams have exactly T = ceil(topk / 64) tiles and the worker size
+// q = max(ceil(N / W), m) is exact; a dense stream has at most max_blocks tiles
+// (its block-table row covers it) and q >= m.  A stream of t tiles meets at
+// most min(W, ceil(t / q) + 1) workers.
+bool merge_ok(const Shape& s, int W, int topk, int max_blocks, int min_tiles, int mode) {
+  if (mode != MLA_MERGE_ON) return false;
+  int64_t tiles, q;
+  if (topk > 0) {
+    tiles = (topk + mla::kPage - 1) / mla::kPage;
+    const int64_t N = (int64_t)s.n_streams * tiles;
+    q = std::max<int64_t>(std::max<int64_t>((N + W - 1) / W, min_tiles), 1);
+  } else {
+    tiles = max_blocks;
+    q = std::max(min_tiles, 1);
+  }
+  return std::min<int64_t>(W, (tiles + q - 1) / q + 1) <= mla::kMergeMaxSplits;
+}
 
 int shape_of(int B, int s_q, int h_q, int h_kv, int topk, Shape* s) {
   if (B < 1 || s_q < 1 || h_q < 1) return fail(MLA_ERR_INVALID_ARG, "B, s_q and h_q must be >= 1 (got %d, %d, %d)", B, s_q, h_q);
@@ -102,7 +126,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 void sizes(const Shape& s, int W, size_t* meta, size_t* part_o, size_t* ws) {
   const size_t max_splits = (size_t)W + (size_t)s.n_streams;
-  *meta = (size_t)mla::meta_words(W, s.n_streams) * sizeof(int32_t);
+  *meta = (size_t)mla::meta_words(W, s.n_streams, s.n_rt) * sizeof(int32_t);
   *part_o = align_up(max_splits * (size_t)s.R * mla::kDV * sizeof(float));
   *ws = *part_o + align_up(max_splits * (size_t)s.R * sizeof(float));
 }
@@ -262,6 +286,8 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
   p.scale_log2 = scale * 1.4426950408889634f;
   const uint64_t pool_bytes = (uint64_t)num_blocks * mla::kPage * (is_fp8 ? mla::kFp8TokenBytes : mla::kBf16TokenBytes);
   p.pool_records = pool_bytes <= 0xFFFFFF00ull ? (uint32_t)pool_bytes : 0u;
+  p.merge = merge_ok(s, W, topk, max_blocks, min_tiles_for(is_fp8, topk, s.n_rt), g_merge_mode) ? 1 : 0;
+  p.arrive = const_cast<int32_t*>(metadata) + mla::meta_arrive(W, s.n_streams);
   hipError_t e = hipSuccess;
   if (g_ev_start && (e = hipEventRecord(g_ev_start, (hipStream_t)stream)) != hipSuccess)
     return hip_fail(e, "decode start event");
@@ -269,8 +295,18 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (g_ev_stop && (e = hipEventRecord(g_ev_stop, (hipStream_t)stream)) != hipSuccess)
     return hip_fail(e, "decode stop event");
-  e = mla::launch_combine(p, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (!p.merge) {
+    e = mla::launch_combine(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return MLA_OK;
+}
+
+MLA_API int mla_set_merge_mode(int mode) {
+  g_err[0] = 0;
+  if (mode != MLA_MERGE_OFF && mode != MLA_MERGE_ON)
+    return fail(MLA_ERR_INVALID_ARG, "merge mode must be %d or %d (got %d)", MLA_MERGE_OFF, MLA_MERGE_ON, mode);
+  g_merge_mode = mode;
   return MLA_OK;
 }
 

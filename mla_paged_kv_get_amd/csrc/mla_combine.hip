@@ -32,28 +32,14 @@ __device__ __forceinline__ void combine_row(const DecodeParams& p, int stream, i
   const int64_t stride = (int64_t)p.R_stream * kDV;
 
   auto write_out = [&](const float4& acc, const float4& acc2, float L) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    bf16x2 a, b, d, e;
-    a.x = (__bf16)acc.x;
-    a.y = (__bf16)acc.y;
-    b.x = (__bf16)acc.z;
-    b.y = (__bf16)acc.w;
-    d.x = (__bf16)acc2.x;
-    d.y = (__bf16)acc2.y;
-    e.x = (__bf16)acc2.z;
-    e.y = (__bf16)acc2.w;
-    *(uint4*)(p.o + (row_base + row) * kDV + c) =
-        make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, d),
-                   __builtin_bit_cast(uint32_t, e));
+    *(uint4*)(p.o + (row_base + row) * kDV + c) = pack_bf16x8(acc, acc2);
     if (c == 0) p.lse[row_base + row] = L;
   };
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f), acc2 = acc;
 
   if (n <= kCombineFused) {
     // Every split's output is loaded together with the lse values, before its
-    // weight is known.  L = ln sum_j exp(lse_j), evaluated around the largest
-    // lse; a split with lse = -inf (empty) has weight 0 and its output is not
-    // used.
+    // weight is known (one memory round trip).
     float lj[kCombineFused];
     float4 v[kCombineFused], v2[kCombineFused];
 #pragma unroll
@@ -62,30 +48,7 @@ __device__ __forceinline__ void combine_row(const DecodeParams& p, int stream, i
       v[k] = k < n ? *(const float4*)(po + k * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
       v2[k] = k < n ? *(const float4*)(po + k * stride + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int k = 0; k < kCombineFused; ++k) mx = fmaxf(mx, lj[k]);
-    if (mx == kNegInf) {
-      write_out(acc, acc2, kNegInf);
-      return;
-    }
-    float sum = 0.f;
-#pragma unroll
-    for (int k = 0; k < kCombineFused; ++k) sum += lj[k] == kNegInf ? 0.f : __expf(lj[k] - mx);
-    const float L = mx + __logf(sum);
-#pragma unroll
-    for (int k = 0; k < kCombineFused; ++k) {
-      if (lj[k] == kNegInf) continue;
-      const float w = __expf(lj[k] - L);
-      acc.x += w * v[k].x;
-      acc.y += w * v[k].y;
-      acc.z += w * v[k].z;
-      acc.w += w * v[k].w;
-      acc2.x += w * v2[k].x;
-      acc2.y += w * v2[k].y;
-      acc2.z += w * v2[k].z;
-      acc2.w += w * v2[k].w;
-    }
+    const float L = lse_merge<kCombineFused>(lj, v, v2, acc, acc2);
     write_out(acc, acc2, L);
     return;
   }
@@ -197,8 +160,14 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_wide_kernel(Decod
   const int s0 = split_off[stream];
   const int n = split_off[stream + 1] - s0;
   if (n == 1) return;  // finished by the decode kernel
-  constexpr float kNegInf = -__builtin_huge_valf();
   const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (n <= kWideBatch) {
+    // few splits after all: wave 0 merges them in one pass, with the same
+    // arithmetic as every other merge of up to 16 splits
+    if (g == 0) combine_row<kWideBatch>(p, stream, s0, n, row);
+    return;
+  }
+  constexpr float kNegInf = -__builtin_huge_valf();
   const int c = lane * 8;
   const float* lse_col = p.part_lse + (int64_t)s0 * p.R_stream + row;
   const float* po = p.part_o + ((int64_t)s0 * p.R_stream + row) * kDV + c;

@@ -790,7 +790,13 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
               *(MLA_LDS f32x4*)(prow + (ct * 32 + 8 * i) * 4) =
                   f32x4{a[4 * i] * inv, a[4 * i + 1] * inv, a[4 * i + 2] * inv, a[4 * i + 3] * inv};
             }
-          if (cv == 0 && lo2 < 32 && rowj < p.R_stream) p.part_lse[(int64_t)sid * p.R_stream + rowj] = lse_v;
+          if (cv == 0 && lo2 < 32 && rowj < p.R_stream) {
+            float* lp = p.part_lse + (int64_t)sid * p.R_stream + rowj;
+            if (p.merge)
+              store_coherent_f32(lp, lse_v);
+            else
+              *lp = lse_v;
+          }
         }
       }
     }
@@ -810,33 +816,36 @@ __global__ __launch_bounds__(kThreads8, 1) void mla_decode_fp8_kernel(DecodePara
         }
       } else {
         // a row that attends nothing in this split (lse = -inf) leaves its
-        // partial output unwritten: the combine gives such a split weight 0
-        // and does not use its output
+        // partial output unwritten: the merge gives such a split weight 0 and
+        // does not use its output
         const float lrow = xrow[to & 63] + xrow[64 + (to & 63)];
         const uint64_t live = __ballot(lrow > 0.f);
-        char* dst = (char*)(p.part_o + ((int64_t)sid * p.R_stream + rt * kRowTile) * kDV);
+        if (p.merge) {
+          merge_split_tile<kThreads8>(p, smem, kOutRowF32, stream, rt, sid, split_off[stream], nsplit, nrows, live,
+                                      wflag, to);
+        } else {
+          char* dst = (char*)(p.part_o + ((int64_t)sid * p.R_stream + rt * kRowTile) * kDV);
 #pragma unroll
-        for (int k = 0; k < kRowTile * kDV * 4 / 16 / kThreads8; ++k) {
-          const int c = k * kThreads8 + to;
-          const int row = c >> 7, off = (c & 127) * 16;
-          if (row < nrows && ((live >> row) & 1u)) *(u32x4*)(dst + row * (kDV * 4) + off) = *(MLA_LDS u32x4*)(smem + row * kOutRowF32 + off);
+          for (int k = 0; k < kRowTile * kDV * 4 / 16 / kThreads8; ++k) {
+            const int c = k * kThreads8 + to;
+            const int row = c >> 7, off = (c & 127) * 16;
+            if (row < nrows && ((live >> row) & 1u)) *(u32x4*)(dst + row * (kDV * 4) + off) = *(MLA_LDS u32x4*)(smem + row * kOutRowF32 + off);
+          }
         }
       }
     }
     // the next piece reuses LDS; after the last one there is nothing to wait for
     if (stream < es && stream + 1 < p.n_streams) __syncthreads();
   }
+  if (p.merge && p.topk == 0) zero_empty_streams<kThreads8>(p, tid);
 }
 
 template <bool SPARSE, bool BUFG>
 hipError_t launch_fp8(const DecodeParams& p, hipStream_t stream) {
-  static bool attr_set = false;
+  static std::atomic<uint64_t> lds_set{0};
   auto kern = mla_decode_fp8_kernel<SPARSE, BUFG>;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = set_lds_limit((const void*)kern, kLdsBytes, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.W * p.n_rt), dim3(kThreads8), kLdsBytes, stream, p);
   return hipGetLastError();
 }

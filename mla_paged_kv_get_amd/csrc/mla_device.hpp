@@ -65,6 +65,117 @@ __device__ __forceinline__ float halves_max(float v) {
   return fmaxf(a, b);
 }
 
+// ---- merging decode (the last split of a row tile merges its stream's splits) ----
+// A split that knows it is not alone cannot hand its partial result to the
+// others through its XCD's L2 (the L2s of the eight XCDs are not coherent with
+// each other, and writing back a whole L2 per workgroup is far too slow), so a
+// merging call writes partials with device-coherent stores (cache policy sc1:
+// written through to memory, as an agent-scope relaxed atomic store is), waits
+// for them, then counts itself in with one agent-scope atomic per (stream, row
+// tile).  The split that counts last reads every split's partial with
+// device-coherent loads, merges them as the combine kernel does and writes o
+// and lse; it also resets the counter, so the metadata serves the next call.
+constexpr int kCpolSc1 = 16;            // buffer instruction cache policy: sc1
+constexpr int kRawBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data, no swizzle
+
+__device__ __forceinline__ void store_coherent_f32(float* ptr, float v) {
+  __hip_atomic_store((int*)ptr, __builtin_bit_cast(int, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent_f32(const float* ptr) {
+  return __builtin_bit_cast(float, __hip_atomic_load((int*)ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Writes a row tile's partial output (staged in LDS as fp32 rows of `pitch`
+// bytes; only rows whose bit is set in `live`, the rest attended nothing) to the
+// workspace, counts the split in, and, in the last split of the row tile to
+// arrive, merges the stream's nsplit <= kMergeMaxSplits splits (first split id
+// s0) into o and lse.  Every thread of the 512-thread workgroup calls it;
+// `flag` is one int of LDS.  The split's lse values were written before with
+// store_coherent_f32.
+template <int kThreadsWG>
+__device__ __forceinline__ void merge_split_tile(const DecodeParams& p, MLA_LDS const char* stage, int pitch,
+                                                 int stream, int rt, int sid, int s0, int nsplit, int nrows,
+                                                 uint64_t live, MLA_LDS int32_t* flag, int tid) {
+  constexpr float kNegInf = -__builtin_huge_valf();
+  const int64_t R = p.R_stream;
+  {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.part_o + ((int64_t)sid * R + rt * kRowTile) * kDV), 0, nrows * kDV * 4, kRawBufferFlags);
+#pragma unroll
+    for (int k = 0; k < kRowTile * kDV * 4 / 16 / kThreadsWG; ++k) {
+      const int c = k * kThreadsWG + tid;
+      const int row = c >> 7, off = (c & 127) * 16;
+      if (row < nrows && ((live >> row) & 1u))
+        __builtin_amdgcn_raw_buffer_store_b128(*(MLA_LDS const u32x4*)(stage + row * pitch + off), rs,
+                                               row * kDV * 4 + off, 0, kCpolSc1);
+    }
+  }
+  // every store of this wave (partial rows and lse values) has completed
+  // before the barrier, so every store of the workgroup before the count
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int32_t* cnt = p.arrive + (int64_t)stream * p.n_rt + rt;
+  if (tid == 0) *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*flag != nsplit - 1) return;  // another split merges
+  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const __amdgpu_buffer_rsrc_t ps = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.part_o + (int64_t)s0 * R * kDV), 0, (int)(nsplit * R * kDV * 4), kRawBufferFlags);
+  const int64_t row_base = (int64_t)stream * R;
+  // 64 rows x 64 pieces of 8 columns: four pieces per thread at a time, all
+  // their loads in flight together
+  constexpr int kBatch = 4;
+#pragma unroll 1
+  for (int i0 = 0; i0 < kRowTile * (kDV / 8); i0 += kBatch * kThreadsWG) {
+    float lj[kBatch][kMergeMaxSplits];
+    float4 v[kBatch][kMergeMaxSplits], v2[kBatch][kMergeMaxSplits];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int i = i0 + t * kThreadsWG + tid;
+      const int row = i >> 6, c8 = (i & 63) * 8;
+      const int rowj = rt * kRowTile + row;
+#pragma unroll
+      for (int j = 0; j < kMergeMaxSplits; ++j) {
+        const bool ok = j < nsplit && row < nrows;
+        const uint32_t off = (uint32_t)(((int64_t)j * R + rowj) * kDV + c8) * 4u;
+        lj[t][j] = ok ? load_coherent_f32(p.part_lse + (int64_t)(s0 + j) * R + rowj) : kNegInf;
+        v[t][j] = ok ? __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ps, off, 0, kCpolSc1))
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        v2[t][j] = ok ? __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ps, off + 16u, 0, kCpolSc1))
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int i = i0 + t * kThreadsWG + tid;
+      const int row = i >> 6, c8 = (i & 63) * 8;
+      if (row >= nrows) continue;
+      const int rowj = rt * kRowTile + row;
+      float4 acc, acc2;
+      const float L = lse_merge<kMergeMaxSplits>(lj[t], v[t], v2[t], acc, acc2);
+      *(uint4*)(p.o + (row_base + rowj) * kDV + c8) = pack_bf16x8(acc, acc2);
+      if (c8 == 0) p.lse[row_base + rowj] = L;
+    }
+  }
+}
+
+// Merging call, dense cache: streams with no tiles (empty requests) have no
+// split to write them, so workgroup g gives streams g, g + grid, ... that are
+// empty o = 0 and lse = -inf (the combine kernel does this otherwise).
+template <int kThreadsWG>
+__device__ __forceinline__ void zero_empty_streams(const DecodeParams& p, int tid) {
+  const int32_t* first = p.meta + meta_tile_first(p.W, p.n_streams);
+  for (int s = blockIdx.x; s < p.n_streams; s += gridDim.x) {
+    if (first[s + 1] != first[s]) continue;
+    const int64_t row_base = (int64_t)s * p.R_stream;
+    for (int i = tid; i < p.R_stream * (kDV / 8); i += kThreadsWG) {
+      const int row = i >> 6, c8 = (i & 63) * 8;
+      *(uint4*)(p.o + (row_base + row) * kDV + c8) = make_uint4(0u, 0u, 0u, 0u);
+      if (c8 == 0) p.lse[row_base + row] = -__builtin_huge_valf();
+    }
+  }
+}
+
 __device__ __forceinline__ float pick_scale(const u32x4& s, int i) {
   const uint32_t v = i == 0 ? s.x : i == 1 ? s.y : i == 2 ? s.z : s.w;
   return __builtin_bit_cast(float, v);

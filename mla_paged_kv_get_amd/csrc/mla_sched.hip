@@ -149,6 +149,13 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(const int32_t*
       g_first[i] = first[i];
       g_split[i] = split_off[i];
     }
+  // arrival counters of merging decode calls start at zero
+  {
+    const int R = topk > 0 ? h_q : s_q * h_q;
+    const int64_t n_cnt = (int64_t)n * ((R + kRowTile - 1) / kRowTile);
+    int32_t* arrive = meta + meta_arrive(W, n);
+    for (int64_t i = tid; i < n_cnt; i += kSchedThreads) arrive[i] = 0;
+  }
   if (tid == 0) {
     int32_t h[kMetaHeader] = {0};
     h[MH_MAGIC] = kMetaMagic;

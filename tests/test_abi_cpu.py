@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     assert set(syms) == {"mla_get_metadata_size", "mla_get_metadata", "mla_decode_with_kvcache", "mla_last_error",
                          "mla_debug_dequant_fp8", "mla_set_decode_kernel_events",
                          "mla_sparse_prefill_workspace_size", "mla_sparse_prefill",
-                         "mla_decode_with_kvcache_noalloc"}
+                         "mla_decode_with_kvcache_noalloc", "mla_set_merge_mode"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -60,13 +60,25 @@ def test_metadata_and_workspace_sizes(L):
     rc, mb, wb, w = sizes(L, 64, 1, 128, W=128)
     assert rc == 0 and w == 128
     n_streams, R = 64, 128
-    assert mb == 4 * (16 + 8 * 128 + 2 * (n_streams + 1))
+    # header, 8 words per worker, split offsets and tile starts, one arrival
+    # counter per (stream, 64-row tile)
+    assert mb == 4 * (16 + 8 * 128 + 2 * (n_streams + 1) + n_streams * 2)
     splits = 128 + n_streams
     part_o = -(-splits * R * 512 * 4 // 256) * 256
     assert wb == part_o + (-(-splits * R * 4 // 256) * 256)
     rc, mb, wb, w = sizes(L, 8, 2, 64, topk=2048, W=256)
     assert rc == 0
-    assert mb == 4 * (16 + 8 * 256 + 2 * (16 + 1))
+    assert mb == 4 * (16 + 8 * 256 + 2 * (16 + 1) + 16 * 1)
+    rc, mb, wb, w = sizes(L, 3, 65, 2, W=16)  # 130 rows per stream: 3 row tiles
+    assert rc == 0 and mb == 4 * (16 + 8 * 16 + 2 * (3 + 1) + 3 * 3)
+
+
+def test_merge_mode_values(L):
+    L.mla_set_merge_mode.argtypes = [ctypes.c_int]
+    assert L.mla_set_merge_mode(2) == -1 and "merge mode" in L.mla_last_error().decode()
+    assert L.mla_set_merge_mode(-1) == -1
+    for m in (1, 0):  # ends on the default (off)
+        assert L.mla_set_merge_mode(m) == 0
 
 
 def test_size_call_rejects_bad_shapes(L):
