@@ -135,3 +135,24 @@ def test_default_mode_launches_the_combine():
     o, lse = flat(o0, l0)
     o_ref, lse_ref = oracle.problem_decode(prob)
     compare(o, lse, o_ref, lse_ref, "tiny workload, combine kernel")
+
+
+@pytest.mark.parametrize("kw,W", [
+    (dict(B=2, s_q=1, h_q=64, seqlens=[700, 200]), 0),                      # dense: max_blocks 11, splits of 2 tiles
+    (dict(B=2, s_q=1, h_q=64, seqlens=[3000, 1500], topk=1024), 64),        # sparse: 16 tiles per stream, q = 2
+], ids=["dense long rows", "sparse many splits"])
+def test_merge_mode_falls_back_where_unproven(kw, W):
+    """Where the host cannot prove at most 4 splits per stream, a call in merge
+    mode runs the combine kernel: poisoned arrival counters change nothing."""
+    import mla_paged_kv_get_amd as mla
+
+    prob = mi.make_problem("merge fallback", seed=150, **kw)
+    d = to_device(prob)
+    meta = mla.mla_get_metadata(d["cache_seqlens"], prob.s_q, prob.h_q, 1, prob.topk, prob.is_fp8, W)
+    mla.mla_set_merge_mode(mla.MLA_MERGE_OFF)
+    o0, l0 = _call(mla, prob, d, meta, False)
+    mla.mla_set_merge_mode(mla.MLA_MERGE_ON)
+    _arrive_slice(prob, meta).fill_(1000)
+    o1, l1 = _call(mla, prob, d, meta, False)
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+    assert (_arrive_slice(prob, meta) == 1000).all()
