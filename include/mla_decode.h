@@ -118,7 +118,9 @@ MLA_API int mla_get_metadata(const int32_t* cache_seqlens, int B, int s_q, int h
  *                  row j % 64 of page block_table[b, j / 64]
  *   cache_seqlens  device int32 [B] (the same values the metadata was built from)
  *   softmax_scale  <= 0 selects 1 / sqrt(576)
- *   metadata       from mla_get_metadata with the same shape and num_workers
+ *   metadata       from mla_get_metadata with the same shape and num_workers;
+ *                  read, and in the merging mode (mla_set_merge_mode) its
+ *                  arrival counters are updated and left at zero
  *   indices        device int32 [B, s_q, topk] when topk > 0, else NULL
  *   causal         0 or 1; 1 (dense only, else MLA_ERR_INVALID_ARG) masks the
  *                  attention of speculative query tokens: the s_q query tokens
@@ -141,7 +143,7 @@ MLA_API int mla_get_metadata(const int32_t* cache_seqlens, int B, int s_q, int h
  */
 MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_blocks, const int32_t* block_table,
                                     int max_blocks, const int32_t* cache_seqlens, int B, int s_q, int h_q, int h_kv,
-                                    int d_qk, int d_v, float softmax_scale, const int32_t* metadata,
+                                    int d_qk, int d_v, float softmax_scale, int32_t* metadata,
                                     size_t metadata_bytes, int num_workers, const int32_t* indices, int topk,
                                     int is_fp8, int causal, void* workspace, size_t workspace_bytes, void* o,
                                     float* lse, void* stream);
@@ -167,7 +169,7 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
 MLA_API int mla_decode_with_kvcache_noalloc(const void* q, const void* kvcache, int64_t num_blocks,
                                             const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
                                             int B, int s_q, int h_q, int h_kv, int d_qk, int d_v, float softmax_scale,
-                                            const int32_t* metadata, size_t metadata_bytes, int num_workers,
+                                            int32_t* metadata, size_t metadata_bytes, int num_workers,
                                             const int32_t* indices, int topk, int is_fp8, int causal, void* o,
                                             float* lse, void* stream);
 

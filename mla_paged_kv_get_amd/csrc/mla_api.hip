@@ -230,7 +230,7 @@ MLA_API int mla_get_metadata(const int32_t* cache_seqlens, int B, int s_q, int h
 
 MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t num_blocks, const int32_t* block_table,
                                     int max_blocks, const int32_t* cache_seqlens, int B, int s_q, int h_q, int h_kv,
-                                    int d_qk, int d_v, float softmax_scale, const int32_t* metadata,
+                                    int d_qk, int d_v, float softmax_scale, int32_t* metadata,
                                     size_t metadata_bytes, int num_workers, const int32_t* indices, int topk,
                                     int is_fp8, int causal, void* workspace, size_t workspace_bytes, void* o,
                                     float* lse, void* stream) {
@@ -287,7 +287,7 @@ MLA_API int mla_decode_with_kvcache(const void* q, const void* kvcache, int64_t 
   const uint64_t pool_bytes = (uint64_t)num_blocks * mla::kPage * (is_fp8 ? mla::kFp8TokenBytes : mla::kBf16TokenBytes);
   p.pool_records = pool_bytes <= 0xFFFFFF00ull ? (uint32_t)pool_bytes : 0u;
   p.merge = merge_ok(s, W, topk, max_blocks, min_tiles_for(is_fp8, topk, s.n_rt), g_merge_mode) ? 1 : 0;
-  p.arrive = const_cast<int32_t*>(metadata) + mla::meta_arrive(W, s.n_streams);
+  p.arrive = metadata + mla::meta_arrive(W, s.n_streams);
   hipError_t e = hipSuccess;
   if (g_ev_start && (e = hipEventRecord(g_ev_start, (hipStream_t)stream)) != hipSuccess)
     return hip_fail(e, "decode start event");
@@ -313,7 +313,7 @@ MLA_API int mla_set_merge_mode(int mode) {
 MLA_API int mla_decode_with_kvcache_noalloc(const void* q, const void* kvcache, int64_t num_blocks,
                                             const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
                                             int B, int s_q, int h_q, int h_kv, int d_qk, int d_v, float softmax_scale,
-                                            const int32_t* metadata, size_t metadata_bytes, int num_workers,
+                                            int32_t* metadata, size_t metadata_bytes, int num_workers,
                                             const int32_t* indices, int topk, int is_fp8, int causal, void* o,
                                             float* lse, void* stream) {
   g_err[0] = 0;
