@@ -89,6 +89,17 @@ def test_merged_equals_combine_kernel_and_oracle(case, W):
     o, lse = flat(o1, l1)
     o_ref, lse_ref = oracle.problem_decode(prob, None, causal)
     compare(o, lse, o_ref, lse_ref, "merged " + prob.name)
+    # new queries on the same metadata and workspace: a merge that read a
+    # split's partial left from the previous call would mix the two
+    d2 = dict(d)
+    d2["q"] = torch.flip(d["q"], dims=[2]).contiguous()
+    mla.mla_set_merge_mode(mla.MLA_MERGE_OFF)
+    o3, l3 = _call(mla, prob, d2, meta, causal, ws=ws)
+    mla.mla_set_merge_mode(mla.MLA_MERGE_ON)
+    _call(mla, prob, d, meta, causal, ws=ws)
+    o4, l4 = _call(mla, prob, d2, meta, causal, ws=ws)
+    assert torch.equal(o4, o3) and torch.equal(l4, l3), "merged call used partials of an earlier call"
+    assert not torch.equal(o3, o0)
 
 
 def test_merge_is_taken_and_counted():
