@@ -41,3 +41,27 @@ def test_noalloc_matches_workspace_entry_point_on_two_calls():
         o, lse = flat(o_na, lse_na)
         o_ref, lse_ref = oracle.problem_decode(prob)
         compare(o, lse, o_ref, lse_ref, prob.name)
+
+
+def test_noalloc_in_merge_mode():
+    """The allocation-free entry point with the decode kernel merging the splits
+    (its partials then live in the static scratch too): the same bits as the
+    workspace entry point with the combine kernel."""
+    import mla_paged_kv_get_amd as mla
+
+    prob = mi.make_problem("noalloc: dense bf16 merged", 3, 1, 64, [200, 64, 130], seed=203)
+    say("[gpu] %s" % prob.name)
+    d = to_device(prob)
+    meta = mla.mla_get_metadata(d["cache_seqlens"], prob.s_q, prob.h_q, 1, 0, False, 0)
+    o_ws, lse_ws = mla.mla_decode_with_kvcache(d["q"], d["kvcache"], d["block_table"], d["cache_seqlens"], 512, meta)
+    mla.mla_set_merge_mode(mla.MLA_MERGE_ON)
+    try:
+        o_na = torch.empty_like(o_ws)
+        lse_na = torch.empty_like(lse_ws)
+        mla.mla_decode_with_kvcache_noalloc(d["q"], d["kvcache"], d["block_table"], d["cache_seqlens"], 512, meta,
+                                            o_na, lse_na)
+        torch.cuda.synchronize()
+    finally:
+        mla.mla_set_merge_mode(mla.MLA_MERGE_OFF)
+    assert meta.total_splits() > prob.B
+    assert torch.equal(o_na, o_ws) and torch.equal(lse_na, lse_ws)
