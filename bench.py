@@ -1,7 +1,7 @@
 """Benchmark of MLA decode over a paged latent KV cache on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 2,3,4,5]
-                [--no-cpu-baseline] [--calibrate-copy]
+                [--no-cpu-baseline] [--calibrate-copy] [--prefill] [--merge]
 
 A step is one pass of the whole decode path over one batch of synthetic input
 already resident in HBM: the scheduler kernel (mla_get_metadata) and the decode
@@ -77,6 +77,9 @@ def parse():
                     help="also time the sparse prefill call (s_q 2048 query tokens, h_q 128, s_kv 8192, topk 2048)")
     ap.add_argument("--no-headline", action="store_true",
                     help="run only the --workloads listed (the first one is reported); for per-workload profiles")
+    ap.add_argument("--merge", action="store_true",
+                    help="also compare where split results are merged (combine kernel / decode kernel's last split) "
+                         "on small shapes and workloads 1 and 4, with the two modes' calls alternated")
     ap.add_argument("--no-calls", action="store_true",
                     help="skip the separate warm/cold call timings (for kernel traces of the timed steps alone)")
     return ap.parse_args()
@@ -337,6 +340,74 @@ def measure_prefill(steps: int, warmup: int):
                 frac_mfma=round(tflops / PEAK_BF16_TFLOPS, 4))
 
 
+MERGE_SHAPES = [
+    dict(name="dense bf16 B=4 h_q=64 300 tokens", B=4, s_q=1, h_q=64, seqlens=[300] * 4),
+    dict(name="dense bf16 B=8 h_q=128 512 tokens", B=8, s_q=1, h_q=128, seqlens=[512] * 8),
+    dict(name="dense fp8 B=16 h_q=128 640 tokens", B=16, s_q=1, h_q=128, seqlens=[640] * 16, is_fp8=True),
+    dict(name="sparse fp8 B=32 h_q=128 topk 512", B=32, s_q=1, h_q=128, seqlens=[8192] * 32, topk=512, is_fp8=True),
+]
+
+
+def measure_merge(rounds: int = 30, per: int = 3):
+    """Decode calls with the combine kernel (MLA_MERGE_OFF) and with the decode
+    kernel merging (MLA_MERGE_ON), alternated in groups of `per` calls so that
+    both modes share the clock state; median call time of each (an event pair
+    around each group, behind a GPU spin), and whether the outputs are
+    bit-identical."""
+    import torch
+
+    import mla_inputs as mi
+    import mla_paged_kv_get_amd as mla
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    probs = [mi.config(1)]
+    for sh in MERGE_SHAPES:
+        c = dict(sh)
+        probs.append(mi.make_problem(c.pop("name"), seed=7, **c))
+    probs.append(mi.config(4))
+    out = []
+    for prob in probs:
+        q, kv, bt, sl = prob.q.to(dev), prob.kvcache.to(dev), prob.block_table.to(dev), prob.cache_seqlens.to(dev)
+        idx = None if prob.indices is None else prob.indices.to(dev)
+        meta = mla.mla_get_metadata(sl, prob.s_q, prob.h_q, 1, prob.topk, prob.is_fp8)
+        ws = torch.empty(meta.workspace_bytes, dtype=torch.uint8, device=dev)
+        o_buf = torch.empty((prob.B, prob.s_q, prob.h_q, 512), dtype=torch.bfloat16, device=dev)
+        l_buf = torch.empty((prob.B, prob.s_q, prob.h_q), dtype=torch.float32, device=dev)
+        res, times = {}, {0: [], 1: []}
+
+        def call():
+            return mla.mla_decode_with_kvcache(q, kv, bt, sl, 512, meta, idx, prob.is_fp8, prob.softmax_scale, ws,
+                                               o_buf, l_buf)
+
+        try:
+            for mode in (0, 1):
+                mla.mla_set_merge_mode(mode)
+                o, l = call()
+                torch.cuda.synchronize()
+                res[mode] = (o.clone(), l.clone())
+            for r in range(rounds):
+                for mode in ((0, 1) if r % 2 == 0 else (1, 0)):
+                    mla.mla_set_merge_mode(mode)
+                    torch.cuda._sleep(int(300 * per * 2500))
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(per):
+                        call()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    times[mode].append(e0.elapsed_time(e1) * 1e3 / per)
+        finally:
+            mla.mla_set_merge_mode(mla.MLA_MERGE_OFF)
+        same = torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+        med = {m: sorted(t)[len(t) // 2] for m, t in times.items()}
+        out.append(dict(name=prob.name, call_us_combine_kernel=round(med[0], 2), call_us_merged=round(med[1], 2),
+                        splits=meta.total_splits(), bit_identical=same))
+        del q, kv, bt, sl, idx, ws, o_buf, l_buf
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -393,6 +464,14 @@ def main():
         print("[bench] %s: call %.1f us (%.1f TFLOP/s, %.1f %% of MFMA peak)" % (
             pf["name"], pf["call_us"], pf["tflops"], 100 * pf["frac_mfma"]), file=sys.stderr, flush=True)
         line["workloads"]["prefill"] = pf
+    if args.merge:
+        mg = measure_merge()
+        for m in mg:
+            print("[bench] merge %s: decode call %.2f us with the combine kernel, %.2f us merged in the decode kernel "
+                  "(%d splits, %s)" % (m["name"], m["call_us_combine_kernel"], m["call_us_merged"], m["splits"],
+                                       "bit-identical" if m["bit_identical"] else "OUTPUTS DIFFER"),
+                  file=sys.stderr, flush=True)
+        line["merge"] = mg
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head_prob)
     print(json.dumps(line))
