@@ -178,3 +178,32 @@ def test_noalloc_refuses_shapes_beyond_its_scratch(L):
            ctypes.c_float(0.0), P(0x5000), ctypes.c_size_t(1 << 30), 256, None, 0, 0, 0, P(0x7000), P(0x8000), None)
     assert rc == -2
     assert "scratch" in L.mla_last_error().decode()
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/mla_decode.h is a C header: a C99 translation unit that calls
+    every declared entry point compiles without warnings (gcc, syntax only)."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not installed")
+    src = tmp_path / "use_header.c"
+    src.write_text("""#include "mla_decode.h"
+int main(void) {
+  size_t a = 0, b = 0;
+  int w = 0;
+  int rc = mla_get_metadata_size(1, 1, 16, 1, 0, 8, &a, &b, &w);
+  rc |= mla_set_merge_mode(MLA_MERGE_OFF);
+  rc |= mla_set_decode_kernel_events(NULL, NULL);
+  (void)mla_last_error();
+  (void)mla_get_metadata; (void)mla_decode_with_kvcache; (void)mla_decode_with_kvcache_noalloc;
+  (void)mla_debug_dequant_fp8; (void)mla_sparse_prefill; (void)mla_sparse_prefill_workspace_size;
+  return rc;
+}
+""")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", inc, "-fsyntax-only", str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
